@@ -1,0 +1,204 @@
+"""ctypes binding of libckl (include/ckl.h).
+
+Argument marshalling only: every step of the loss runs inside the HIP library.
+PyTorch provides device memory and the current stream.  If libckl.so has not
+been built, loading fails with an error: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libckl.so")
+
+CKL_OK = 0
+CKL_ERR_INVALID_ARG = 1
+CKL_ERR_UNSUPPORTED = 2
+CKL_ERR_WORKSPACE = 3
+CKL_ERR_BAD_INDEX = 4
+CKL_ERR_HIP = 5
+CKL_F32 = 0
+CKL_BF16 = 1
+
+EXPORTED = (
+    "ckl_workspace_size",
+    "ckl_forward",
+    "ckl_backward",
+    "ckl_backward_plan",
+    "ckl_status_string",
+    "ckl_last_error",
+    "ckl_version",
+)
+
+
+class CklError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ckl status {status}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32),
+        ("dh_dtype", ctypes.c_int32),
+        ("dw_dtype", ctypes.c_int32),
+        ("validate", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libckl.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libckl.so not found at {p}: build it with "
+                           "`python -m chunked_kl_loss_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)
+    P = ctypes.POINTER(Problem)
+    lib.ckl_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ckl_workspace_size.restype = i32
+    lib.ckl_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ckl_forward.restype = i32
+    lib.ckl_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ckl_backward.restype = i32
+    lib.ckl_backward_plan.argtypes = [P, i64p]
+    lib.ckl_backward_plan.restype = i32
+    lib.ckl_status_string.argtypes = [i32]
+    lib.ckl_status_string.restype = ctypes.c_char_p
+    lib.ckl_last_error.argtypes = []
+    lib.ckl_last_error.restype = ctypes.c_char_p
+    lib.ckl_version.argtypes = []
+    lib.ckl_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(status: int, lib=None) -> None:
+    if status != CKL_OK:
+        lib = lib or load_library()
+        raise CklError(status, lib.ckl_last_error().decode())
+
+
+def make_problem(T, d, V, K, chunk, in_dtype=CKL_BF16, dh_dtype=None, dw_dtype=CKL_F32, validate=False) -> Problem:
+    return Problem(int(T), int(d), int(V), int(K), int(chunk), int(in_dtype),
+                   int(in_dtype if dh_dtype is None else dh_dtype), int(dw_dtype), int(bool(validate)))
+
+
+def workspace_size(prob: Problem, which: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    check(lib.ckl_workspace_size(ctypes.byref(prob), int(which), ctypes.byref(out)), lib)
+    return int(out.value)
+
+
+def backward_plan(prob: Problem):
+    lib = load_library()
+    out = (ctypes.c_int64 * 4)()
+    check(lib.ckl_backward_plan(ctypes.byref(prob), out), lib)
+    return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3])
+
+
+# ------------------------------------------------------------ torch layer --
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return CKL_BF16
+    if dt == torch.float32:
+        return CKL_F32
+    raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.bfloat16 if code == CKL_BF16 else torch.float32
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_inputs(H, W, idx, tlogit, mask):
+    torch = _torch()
+    if not (H.is_cuda and W.is_cuda and idx.is_cuda and tlogit.is_cuda):
+        raise ValueError("H, W, idx and tlogit must be GPU tensors")
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1] or H.dtype != W.dtype:
+        raise ValueError("H [T, d] and W [V, d] must share d and dtype")
+    if idx.shape != tlogit.shape or idx.dim() != 2 or idx.shape[0] != H.shape[0]:
+        raise ValueError("idx and tlogit must be [T, K]")
+    if idx.dtype != torch.int32 or tlogit.dtype != torch.float32:
+        raise TypeError("idx must be int32 and tlogit float32")
+    for name, t in (("H", H), ("W", W), ("idx", idx), ("tlogit", tlogit)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if mask is not None:
+        if mask.shape != (H.shape[0],) or mask.dtype not in (torch.uint8, torch.bool) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8/bool [T] tensor")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = False,
+            want_row_loss: bool = False):
+    """Returns (loss [1] float32, lse [T] float32, row_loss [T] or None)."""
+    torch = _torch()
+    _check_inputs(H, W, idx, tlogit, mask)
+    T, d = H.shape
+    V, K = W.shape[0], idx.shape[1]
+    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate)
+    lib = load_library()
+    ws_bytes = workspace_size(prob, 0)
+    dev = H.device
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    m = mask.view(torch.uint8) if mask is not None else None
+    check(lib.ckl_forward(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlogit), _ptr(m),
+                          _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
+    return loss, lse, row_loss
+
+
+def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh_dtype=None,
+             dw_dtype=None, validate: bool = False):
+    """Returns (dH, dW) of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
+    torch = _torch()
+    _check_inputs(H, W, idx, tlogit, mask)
+    T, d = H.shape
+    V, K = W.shape[0], idx.shape[1]
+    in_code = _dtype_code(H.dtype)
+    dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
+    dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate)
+    lib = load_library()
+    ws_bytes = workspace_size(prob, 1)
+    dev = H.device
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dH = torch.empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
+    dW = torch.empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
+    m = mask.view(torch.uint8) if mask is not None else None
+    if grad_loss is not None:
+        grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    check(lib.ckl_backward(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlogit), _ptr(m), _ptr(lse),
+                           _ptr(grad_loss), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
+    return dH, dW

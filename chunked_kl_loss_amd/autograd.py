@@ -1,0 +1,32 @@
+"""torch.autograd wrapper: the forward saves (H, W, idx, tlogit, mask, lse) and
+the backward recomputes the logit tiles inside libckl."""
+from __future__ import annotations
+
+import torch
+
+from . import _binding
+
+
+class ChunkedKLLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048):
+        loss, lse, _ = _binding.forward(H, W, idx, tlogit, mask, chunk=chunk)
+        ctx.save_for_backward(H, W, idx, tlogit, lse, mask if mask is not None else torch.empty(0))
+        ctx.has_mask = mask is not None
+        ctx.chunk = chunk
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, grad):
+        H, W, idx, tlogit, lse, mask = ctx.saved_tensors
+        mask = mask if ctx.has_mask else None
+        g = grad.reshape(1).to(torch.float32)
+        dH, dW = _binding.backward(H, W, idx, tlogit, mask, lse, g, chunk=ctx.chunk,
+                                   dh_dtype=H.dtype, dw_dtype=W.dtype)
+        return dH, dW, None, None, None, None
+
+
+def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048):
+    """Mean forward KL(teacher || student) over unmasked rows, differentiable
+    with respect to H and W."""
+    return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk)

@@ -1,0 +1,329 @@
+// Host side of libckl: argument checks, workspace planning and the launch
+// sequence behind the C ABI declared in include/ckl.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ckl.h"
+#include "ckl_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ckl_status fail(ckl_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ckl_status fail(ckl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ckl_status hip_fail(hipError_t e, const char* what) {
+  return fail(CKL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                         \
+  do {                                              \
+    hipError_t e__ = (expr);                        \
+    if (e__ != hipSuccess) return hip_fail(e__, what); \
+  } while (0)
+
+constexpr int64_t kMaxK = 4096;
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+constexpr int kTargetWorkgroups = 2048;  // fused kernels: row blocks x vocabulary splits
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int64_t T, d, V, K;
+  int in_bf16;
+  int64_t esz;
+  int64_t BM, BN;  // logit tile: vocabulary rows x token rows
+  int64_t Tp, Vp;
+  // forward
+  int64_t f_splits, f_tps;
+  // backward G blocks
+  int64_t Tc, Vc, nT, nV;
+};
+
+// Vocabulary splits of the fused kernels: enough workgroups to fill the chip
+// several times while every split keeps a run of tiles (the teacher cursors
+// advance monotonically along a split).
+void pick_splits(int64_t row_blocks, int64_t vtiles, int64_t* splits, int64_t* tps) {
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(vtiles, ceil_div(kTargetWorkgroups, row_blocks)));
+  *tps = ceil_div(vtiles, s);
+  *splits = ceil_div(vtiles, *tps);
+}
+
+ckl_status check_problem(const ckl_problem* p) {
+  if (!p) return fail(CKL_ERR_INVALID_ARG, "problem is NULL");
+  if (p->T < 1 || p->T > kMaxRows) return fail(CKL_ERR_INVALID_ARG, "T=%lld out of range [1, 2^30]", (long long)p->T);
+  if (p->V < 1 || p->V > kMaxRows) return fail(CKL_ERR_INVALID_ARG, "V=%lld out of range [1, 2^30]", (long long)p->V);
+  if (p->d < 8 || p->d % 8 != 0) return fail(CKL_ERR_INVALID_ARG, "d=%lld must be a positive multiple of 8", (long long)p->d);
+  if (p->d > 65536) return fail(CKL_ERR_UNSUPPORTED, "d=%lld exceeds 65536", (long long)p->d);
+  if (p->K < 1 || p->K > p->V) return fail(CKL_ERR_INVALID_ARG, "K=%lld must satisfy 1 <= K <= V", (long long)p->K);
+  if (p->K > kMaxK) return fail(CKL_ERR_UNSUPPORTED, "K=%lld exceeds %lld", (long long)p->K, (long long)kMaxK);
+  if (p->T * p->K >= ((int64_t)1 << 31)) return fail(CKL_ERR_UNSUPPORTED, "T*K must stay below 2^31");
+  if (p->chunk < 1) return fail(CKL_ERR_INVALID_ARG, "chunk=%lld must be >= 1", (long long)p->chunk);
+  auto dt_ok = [](int32_t t) { return t == CKL_F32 || t == CKL_BF16; };
+  if (!dt_ok(p->in_dtype) || !dt_ok(p->dh_dtype) || !dt_ok(p->dw_dtype))
+    return fail(CKL_ERR_INVALID_ARG, "dtype codes must be CKL_F32 (0) or CKL_BF16 (1)");
+  if (p->validate != 0 && p->validate != 1) return fail(CKL_ERR_INVALID_ARG, "validate must be 0 or 1");
+  return CKL_OK;
+}
+
+Plan make_plan(const ckl_problem* p) {
+  Plan q{};
+  q.T = p->T; q.d = p->d; q.V = p->V; q.K = p->K;
+  q.in_bf16 = p->in_dtype == CKL_BF16;
+  q.esz = q.in_bf16 ? 2 : 4;
+  q.BM = ckl::tile_rows_m();
+  q.BN = ckl::tile_rows_n();
+  q.Tp = round_up(q.T, q.BN);
+  q.Vp = round_up(q.V, q.BM);
+  pick_splits(ceil_div(q.T, q.BN), ceil_div(q.V, q.BM), &q.f_splits, &q.f_tps);
+
+  // G blocks of Tc token rows x Vc vocabulary columns, both stored twice (G and
+  // G^T), within chunk * V elements in total.  Among the admissible shapes pick
+  // the one with the least fp32 read-modify-write of dH (once per extra
+  // vocabulary block) and dW (once per extra token block).
+  const int64_t per_layout = std::max<int64_t>(p->chunk * p->V / 2, q.BM * q.BN);
+  double best = -1.0;
+  for (int64_t nT = 1; nT <= q.Tp / q.BN; ++nT) {
+    const int64_t Tc = round_up(ceil_div(q.Tp, nT), q.BN);
+    if (nT > 1 && Tc == round_up(ceil_div(q.Tp, nT - 1), q.BN)) continue;
+    const int64_t nTr = ceil_div(q.Tp, Tc);
+    int64_t vmax = (per_layout / Tc) / q.BM * q.BM;
+    if (vmax < q.BM) vmax = q.BM;
+    if (Tc * vmax > per_layout && Tc > q.BN) continue;  // only the smallest block may exceed the budget
+    const int64_t nV = ceil_div(q.Vp, vmax);
+    const int64_t Vc = round_up(ceil_div(q.Vp, nV), q.BM);
+    const double cost = (double)(nTr - 1) * q.V * q.d * 8.0 + (double)(nV - 1) * q.T * q.d * 8.0 +
+                        (double)(nTr * nV) * 3.0 * 4.0e6;  // ~launch overhead in byte-equivalents
+    if (best < 0 || cost < best) {
+      best = cost;
+      q.Tc = Tc; q.Vc = Vc; q.nT = nTr; q.nV = ceil_div(q.Vp, Vc);
+    }
+  }
+  return q;
+}
+
+struct FwdWs {
+  size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, total;
+};
+FwdWs fwd_layout(const Plan& q) {
+  FwdWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+  w.idx_s = take(q.T * q.K * 4);
+  w.p_s = take(q.T * q.K * 4);
+  w.zg_s = take(q.T * q.K * 4);
+  w.E = take(q.T * 4);
+  w.M = take(q.T * 4);
+  w.part = take(q.f_splits * q.T * 8);
+  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.N = take(4);
+  w.bad = take(4);
+  w.total = o;
+  return w;
+}
+
+struct BwdWs {
+  size_t idx_s, p_s, M, s, N, bad, Ht, Wt, G, Gt, dH, dW, total;
+};
+BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
+  BwdWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+  w.idx_s = take(q.T * q.K * 4);
+  w.p_s = take(q.T * q.K * 4);
+  w.M = take(q.T * 4);
+  w.s = take(q.Tp * 4);
+  w.N = take(4);
+  w.bad = take(4);
+  w.Ht = take((size_t)q.d * q.Tp * q.esz);
+  w.Wt = take((size_t)q.d * q.Vp * q.esz);
+  w.G = take((size_t)q.Tc * q.Vc * q.esz);
+  w.Gt = take((size_t)q.Tc * q.Vc * q.esz);
+  w.dH = p->dh_dtype == CKL_BF16 ? take((size_t)q.T * q.d * 4) : 0;
+  w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
+  w.total = o;
+  return w;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+ckl_status check_validate_flag(int* bad_dev, hipStream_t st) {
+  int h = 0;
+  HIP_TRY(hipMemcpyAsync(&h, bad_dev, sizeof(int), hipMemcpyDeviceToHost, st), "reading index check flag");
+  HIP_TRY(hipStreamSynchronize(st), "synchronising for the index check");
+  if (h) return fail(CKL_ERR_BAD_INDEX, "teacher indices out of [0, V) or repeated within a row");
+  return CKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!bytes) return fail(CKL_ERR_INVALID_ARG, "bytes is NULL");
+  if (which != 0 && which != 1) return fail(CKL_ERR_INVALID_ARG, "which must be 0 (forward) or 1 (backward)");
+  const Plan q = make_plan(p);
+  *bytes = which == 0 ? fwd_layout(q).total : bwd_layout(q, p).total;
+  return CKL_OK;
+}
+
+ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const int32_t* idx, const float* tlogit,
+                       const uint8_t* mask, float* loss, float* lse, float* row_loss, void* ws, size_t ws_bytes,
+                       void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!H || !W || !idx || !tlogit || !loss || !lse) return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(ws))
+    return fail(CKL_ERR_INVALID_ARG, "H, W, idx, tlogit and ws must be 16-byte aligned");
+  if (((uintptr_t)loss & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)row_loss & 3u))
+    return fail(CKL_ERR_INVALID_ARG, "loss, lse and row_loss must be 4-byte aligned");
+  const Plan q = make_plan(p);
+  const FwdWs w = fwd_layout(q);
+  if (!ws || ws_bytes < w.total)
+    return fail(CKL_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", w.total, ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* b = (char*)ws;
+  int* idx_s = (int*)(b + w.idx_s);
+  float* p_s = (float*)(b + w.p_s);
+  float* zg_s = (float*)(b + w.zg_s);
+  float* E = (float*)(b + w.E);
+  float* M = (float*)(b + w.M);
+  int* N = (int*)(b + w.N);
+  int* bad = (int*)(b + w.bad);
+  const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
+
+  HIP_TRY(ckl::launch_count_mask(mask, T, N, st), "count_mask");
+  if (p->validate) HIP_TRY(ckl::launch_fill_i32(bad, 1, 0, st), "fill");
+  HIP_TRY(ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s, p->validate ? bad : nullptr, st),
+          "teacher_prep");
+  if (p->validate) {
+    s = check_validate_flag(bad, st);
+    if (s != CKL_OK) return s;
+  }
+  HIP_TRY(ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits, (int)q.f_tps, st),
+          "fwd_lse");
+  HIP_TRY(ckl::launch_fwd_finalize(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, E, M, mask, lse, row_loss,
+                                   (double*)(b + w.blk), N, loss, st),
+          "fwd_finalize");
+  return CKL_OK;
+}
+
+ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, const int32_t* idx, const float* tlogit,
+                        const uint8_t* mask, const float* lse, const float* grad_loss, void* dH, void* dW, void* ws,
+                        size_t ws_bytes, void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!H || !W || !idx || !tlogit || !lse || !dH || !dW) return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(dH) || !aligned16(dW) ||
+      !aligned16(ws))
+    return fail(CKL_ERR_INVALID_ARG, "H, W, idx, tlogit, dH, dW and ws must be 16-byte aligned");
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)grad_loss & 3u))
+    return fail(CKL_ERR_INVALID_ARG, "lse and grad_loss must be 4-byte aligned");
+  const Plan q = make_plan(p);
+  const BwdWs w = bwd_layout(q, p);
+  if (!ws || ws_bytes < w.total)
+    return fail(CKL_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", w.total, ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* b = (char*)ws;
+  int* idx_s = (int*)(b + w.idx_s);
+  float* p_s = (float*)(b + w.p_s);
+  float* M = (float*)(b + w.M);
+  float* srow = (float*)(b + w.s);
+  int* N = (int*)(b + w.N);
+  int* bad = (int*)(b + w.bad);
+  void* Ht = b + w.Ht;
+  void* Wt = b + w.Wt;
+  void* G = b + w.G;
+  void* Gt = b + w.Gt;
+  float* dHacc = p->dh_dtype == CKL_BF16 ? (float*)(b + w.dH) : (float*)dH;
+  float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
+  const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
+
+  HIP_TRY(ckl::launch_count_mask(mask, T, N, st), "count_mask");
+  if (p->validate) HIP_TRY(ckl::launch_fill_i32(bad, 1, 0, st), "fill");
+  HIP_TRY(ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, nullptr, M, nullptr, p->validate ? bad : nullptr,
+                                   st),
+          "teacher_prep");
+  if (p->validate) {
+    s = check_validate_flag(bad, st);
+    if (s != CKL_OK) return s;
+  }
+  HIP_TRY(ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st), "row_scale");
+  HIP_TRY(ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp, st), "transpose H");
+  HIP_TRY(ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp, st), "transpose W");
+
+  const char* Htb = (const char*)Ht;
+  const char* Wtb = (const char*)Wt;
+  for (int64_t vb = 0; vb < q.nV; ++vb) {
+    const int64_t vb0 = vb * q.Vc;
+    const int64_t vrows = std::min(q.Vc, q.Vp - vb0);
+    for (int64_t tb = 0; tb < q.nT; ++tb) {
+      const int64_t tb0 = tb * q.Tc;
+      const int64_t trows = std::min(q.Tc, q.Tp - tb0);
+      int64_t splits, tps;
+      pick_splits(trows / q.BN, vrows / q.BM, &splits, &tps);
+      HIP_TRY(ckl::launch_bwd_grad(q.in_bf16, H, W, T, d, V, K, idx_s, p_s, M, lse, srow, (int)tb0, (int)trows,
+                                   (int)vb0, (int)vrows, (int)splits, (int)tps, G, vrows, Gt, trows, st),
+              "bwd_grad");
+      // dH[tb0 .. tb0 + trows) (+)= G W[vb0 .. vb0 + vrows)
+      HIP_TRY(ckl::launch_gemm_store(q.in_bf16, G, vrows, (int)std::min(trows, q.T - tb0), Wtb + vb0 * q.esz, q.Vp, d,
+                                     (int)vrows, dHacc + tb0 * q.d, q.d, vb > 0, st),
+              "gemm dH");
+      // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)
+      HIP_TRY(ckl::launch_gemm_store(q.in_bf16, Gt, trows, (int)std::min(vrows, q.V - vb0), Htb + tb0 * q.esz, q.Tp,
+                                     d, (int)trows, dWacc + vb0 * q.d, q.d, tb > 0, st),
+              "gemm dW");
+    }
+  }
+  if (p->dh_dtype == CKL_BF16) HIP_TRY(ckl::launch_cast_f32_bf16(dHacc, dH, q.T * q.d, st), "cast dH");
+  if (p->dw_dtype == CKL_BF16) HIP_TRY(ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st), "cast dW");
+  return CKL_OK;
+}
+
+ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!out) return fail(CKL_ERR_INVALID_ARG, "out is NULL");
+  const Plan q = make_plan(p);
+  out[0] = q.Tc;
+  out[1] = q.Vc;
+  out[2] = q.nT;
+  out[3] = q.nV;
+  return CKL_OK;
+}
+
+const char* ckl_status_string(ckl_status s) {
+  switch (s) {
+    case CKL_OK: return "ok";
+    case CKL_ERR_INVALID_ARG: return "invalid argument";
+    case CKL_ERR_UNSUPPORTED: return "unsupported problem";
+    case CKL_ERR_WORKSPACE: return "workspace missing or too small";
+    case CKL_ERR_BAD_INDEX: return "teacher index out of range or repeated";
+    case CKL_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ckl_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ckl_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

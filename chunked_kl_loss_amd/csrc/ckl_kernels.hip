@@ -1,0 +1,663 @@
+// gfx950 kernels of libckl: the fused chunked forward-KL loss.
+//
+// Forward (objective section of the README page "Chunked KL loss, running
+// Knowledge Distillation locally in less <6GB VRAM"):
+//   teacher_prep   p = softmax of the K cached logits per row, sorted by
+//                  vocabulary index, with E = sum p log p and M = sum p
+//   fwd_lse        logit tiles z^T = W H^T on MFMA, never stored; per row an
+//                  online base-2 log-sum-exp over the vocabulary tiles of one
+//                  split, and the logits at the teacher indices picked out of
+//                  the accumulators
+//   fwd_finalize   merge the splits into LSE, l_t = E - sum p z_idx + M LSE,
+//                  deterministic masked sum
+// Backward (Full Chunked KL paragraph of the same page: recompute each chunk,
+// apply the closed-form gradient):
+//   bwd_grad       recompute the logit tiles of one G block and turn them into
+//                  G = s (M 2^{z log2 e - LSE log2 e} - p~), rounded once to
+//                  the input dtype, stored as G and G^T
+//   gemm_store     dH (+)= G W and dW (+)= G^T H on the same MFMA main loop
+#include "ckl_kernels.hpp"
+
+#include "ckl_tile.hpp"
+
+namespace ckl {
+
+// ---------------------------------------------------------------- helpers --
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <typename T>
+__device__ __forceinline__ void store2(T* p, float a, float b);
+template <>
+__device__ __forceinline__ void store2<bf16_t>(bf16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+template <>
+__device__ __forceinline__ void store2<float>(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
+// First position k in the ascending row idx_s[0..K) with idx_s[k] >= v.
+__device__ __forceinline__ int lower_bound_row(const int* __restrict__ row, int K, int v) {
+  int lo = 0, hi = K;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// ----------------------------------------------------------- small kernels --
+__global__ void fill_i32_kernel(int* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// N = number of kept rows (mask NULL: all T).  One workgroup, fixed order.
+__global__ __launch_bounds__(1024) void count_mask_kernel(const uint8_t* __restrict__ mask, int T, int* N) {
+  __shared__ int red[1024];
+  int c = 0;
+  if (mask == nullptr) {
+    c = (threadIdx.x == 0) ? T : 0;
+  } else {
+    for (int t = threadIdx.x; t < T; t += 1024) c += mask[t] != 0;
+  }
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *N = red[0];
+}
+
+// s[t] = grad_loss * keep_t / N for t < T, 0 for T <= t < Tp.
+__global__ void row_scale_kernel(const uint8_t* __restrict__ mask, const float* __restrict__ grad_loss,
+                                 const int* __restrict__ N, int T, int Tp, float* __restrict__ s) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= Tp) return;
+  const int n = *N;
+  const float g = grad_loss ? *grad_loss : 1.f;
+  float v = 0.f;
+  if (t < T && n > 0 && (mask == nullptr || mask[t] != 0)) v = g / (float)n;
+  s[t] = v;
+}
+
+// One wavefront per row.  Softmax of the K cached logits (fp32), then a
+// bitonic sort of (idx, p) by idx in LDS.  Optional outputs: E (sum p log p),
+// zero-filled zg.  `bad` collects out-of-range / repeated indices.
+__global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict__ idx, const float* __restrict__ tlogit,
+                                                          int T, int K, int Kp, int V, int* __restrict__ idx_s,
+                                                          float* __restrict__ p_s, float* __restrict__ Erow,
+                                                          float* __restrict__ Mrow, float* __restrict__ zg_s,
+                                                          int* __restrict__ bad) {
+  extern __shared__ int sm_dyn[];
+  int* key = sm_dyn;
+  float* val = reinterpret_cast<float*>(sm_dyn + Kp);
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int* irow = idx + (int64_t)t * K;
+  const float* lrow = tlogit + (int64_t)t * K;
+
+  float mx = -INFINITY;
+  for (int k = lane; k < K; k += 64) mx = fmaxf(mx, lrow[k]);
+  mx = wave_max(mx);
+  float se = 0.f;
+  for (int k = lane; k < K; k += 64) se += expf(lrow[k] - mx);
+  se = wave_sum(se);
+  const float inv = 1.f / se;
+  const float logse = logf(se);
+  float ent = 0.f, mass = 0.f;
+  for (int k = lane; k < Kp; k += 64) {
+    if (k < K) {
+      const float a = lrow[k] - mx;
+      const float p = expf(a) * inv;
+      ent += p * (a - logse);
+      mass += p;
+      key[k] = irow[k];
+      val[k] = p;
+    } else {
+      key[k] = kIdxEnd;
+      val[k] = 0.f;
+    }
+  }
+  ent = wave_sum(ent);
+  mass = wave_sum(mass);
+  __syncthreads();
+  for (int size = 2; size <= Kp; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = lane; i < (Kp >> 1); i += 64) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const int a = key[lo], b = key[hi];
+        if ((a > b) == asc) {
+          key[lo] = b; key[hi] = a;
+          const float va = val[lo];
+          val[lo] = val[hi]; val[hi] = va;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int badl = 0;
+  for (int k = lane; k < K; k += 64) {
+    const int v = key[k];
+    idx_s[(int64_t)t * K + k] = v;
+    p_s[(int64_t)t * K + k] = val[k];
+    if (zg_s) zg_s[(int64_t)t * K + k] = 0.f;
+    if (v < 0 || v >= V || (k + 1 < K && key[k + 1] == v)) badl = 1;
+  }
+  if (bad && badl) atomicOr(bad, 1);
+  if (lane == 0) {
+    if (Erow) Erow[t] = ent;
+    Mrow[t] = mass;
+  }
+}
+
+// ------------------------------------------------------------ forward LSE --
+// grid.x: token blocks of BN rows; grid.y: vocabulary splits of
+// tiles_per_split tiles of BM rows.  Output part[split * T + t] = (m, s):
+// the base-2 log-sum-exp state of row t over the split.
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
+    const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
+    const int* __restrict__ idx_s, float* __restrict__ zg_s, float2* __restrict__ part, int n_vtiles,
+    int tiles_per_split) {
+  using TIn = typename C::TIn;
+  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_m = wave / C::WAVES_N;
+  const int wave_n = wave % C::WAVES_N;
+  const int t0 = blockIdx.x * C::BN;
+  const int split = blockIdx.y;
+  const int vt0 = split * tiles_per_split;
+  const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
+
+  int tok[C::NB], cur[C::NB], nxt[C::NB];
+  float rm[C::NB], rs[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    tok[nb] = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
+    rm[nb] = -INFINITY;
+    rs[nb] = 0.f;
+    cur[nb] = K;
+    nxt[nb] = kIdxEnd;
+    if (tok[nb] < T) {
+      const int* row = idx_s + (int64_t)tok[nb] * K;
+      cur[nb] = lower_bound_row(row, K, vt0 * C::BM);
+      nxt[nb] = cur[nb] < K ? row[cur[nb]] : kIdxEnd;
+    }
+  }
+
+  Tile<C> tile;
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const int v0 = vt * C::BM;
+    tile_mma<C>(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    const int vbase = v0 + wave_m * C::WM;
+    const int vend = min(v0 + C::BM, V);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + mb * 32 + acc_row(r, lane);
+          if (v < V) mx = fmaxf(mx, tile.acc[mb][nb][r] * kLog2e);
+        }
+      const float mn = fmaxf(rm[nb], mx);
+      float ssum = 0.f;
+      if (mn != -INFINITY) {
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + mb * 32 + acc_row(r, lane);
+            if (v < V) ssum += fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn);
+          }
+        rs[nb] = rs[nb] * fast_exp2(rm[nb] - mn) + ssum;
+        rm[nb] = mn;
+      }
+      // logits at the teacher indices of this row that fall in this tile
+      while (nxt[nb] < vend) {
+        const int vl = nxt[nb] - vbase;
+        if (vl >= 0 && vl < C::WM) {
+          const int rr = vl & 31;
+          if (((rr >> 2) & 1) == (lane >> 5)) {
+            const int sel = (vl >> 5) * 16 + (rr >> 3) * 4 + (rr & 3);
+            float val = 0.f;
+#pragma unroll
+            for (int q = 0; q < C::MB * 16; ++q) val = (q == sel) ? tile.acc[q / 16][nb][q % 16] : val;
+            zg_s[(int64_t)tok[nb] * K + cur[nb]] = val;
+          }
+        }
+        ++cur[nb];
+        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok[nb] * K + cur[nb]] : kIdxEnd;
+      }
+    }
+  }
+
+  // lanes l and l ^ 32 hold the same token over different vocabulary rows
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const float om = __shfl_xor(rm[nb], 32);
+    const float os = __shfl_xor(rs[nb], 32);
+    lse2_merge(rm[nb], rs[nb], om, os);
+  }
+  // then across the WAVES_M waves sharing the same tokens
+  float2* red = reinterpret_cast<float2*>(smem);  // [WAVES_M][BN]
+  if (lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+      red[wave_m * C::BN + wave_n * C::WN + nb * 32 + lane] = make_float2(rm[nb], rs[nb]);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < C::BN; i += C::NTHREADS) {
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::WAVES_M; ++w) {
+      const float2 x = red[w * C::BN + i];
+      lse2_merge(m, s, x.x, x.y);
+    }
+    if (t0 + i < T) part[(int64_t)split * T + t0 + i] = make_float2(m, s);
+  }
+}
+
+// One thread per row: LSE from the split states, l_t, masked fp64 block sum.
+__global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restrict__ part, int S, int T, int K,
+                                                           const float* __restrict__ p_s,
+                                                           const float* __restrict__ zg_s,
+                                                           const float* __restrict__ Erow,
+                                                           const float* __restrict__ Mrow,
+                                                           const uint8_t* __restrict__ mask,
+                                                           float* __restrict__ lse_out,
+                                                           float* __restrict__ row_loss,
+                                                           double* __restrict__ blk_sum) {
+  __shared__ double red[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  if (t < T) {
+    const bool keep = mask == nullptr || mask[t] != 0;
+    float lse = 0.f, l = 0.f;
+    if (keep) {
+      float m = -INFINITY, s = 0.f;
+      for (int sp = 0; sp < S; ++sp) {
+        const float2 x = part[(int64_t)sp * T + t];
+        lse2_merge(m, s, x.x, x.y);
+      }
+      lse = (m + fast_log2(s)) * kLn2;
+      double x = 0.0;
+      const float* pr = p_s + (int64_t)t * K;
+      const float* zr = zg_s + (int64_t)t * K;
+      for (int k = 0; k < K; ++k) x += (double)pr[k] * (double)zr[k];
+      const double ld = (double)Erow[t] - x + (double)Mrow[t] * (double)lse;
+      l = (float)ld;
+      contrib = ld;
+    }
+    lse_out[t] = lse;
+    if (row_loss) row_loss[t] = l;
+  }
+  red[threadIdx.x] = contrib;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blk_sum[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const double* __restrict__ blk_sum, int nblk,
+                                                          const int* __restrict__ N, float* __restrict__ loss) {
+  __shared__ double red[256];
+  double a = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) a += blk_sum[i];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = *N;
+    *loss = n > 0 ? (float)(red[0] / (double)n) : 0.f;
+  }
+}
+
+// ----------------------------------------------------- transposes / casts --
+// dst[c * ldd + r] = src[r * C + c] for r < R; 0 for R <= r < Rp.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ src, int R, int C, int Rp,
+                                                            T* __restrict__ dst, int64_t ldd) {
+  __shared__ T tileS[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    T v = T(0.f);
+    if (r < R && c < C) v = src[(int64_t)r * C + c];
+    tileS[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) dst[(int64_t)c * ldd + r] = tileS[tx][i];
+  }
+}
+
+__global__ void cast_f32_bf16_kernel(const float* __restrict__ src, bf16_t* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const uint32_t b = f32_to_bf16_bits(src[i]);
+    reinterpret_cast<uint16_t*>(dst)[i] = (uint16_t)b;
+  }
+}
+
+// ------------------------------------------------------------ backward G --
+// Recomputes the logit tiles of the G block rows [tb0, tb0 + 128 gridDim.x),
+// vocabulary [vb0, vb0 + BM n_vtiles) and writes
+//   G [t - tb0][v - vb0]  (row stride ldG)  and  Gt[v - vb0][t - tb0] (ldGt)
+// with G = s_t (M_t q_t[v] - p~_t[v]); rows t >= T and columns v >= V get 0.
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
+    const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
+    const int* __restrict__ idx_s, const float* __restrict__ p_s, const float* __restrict__ Mrow,
+    const float* __restrict__ lse, const float* __restrict__ srow, int tb0, int vb0, int n_vtiles,
+    int tiles_per_split, typename C::TIn* __restrict__ G, int64_t ldG, typename C::TIn* __restrict__ Gt,
+    int64_t ldGt) {
+  using TIn = typename C::TIn;
+  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_m = wave / C::WAVES_N;
+  const int wave_n = wave % C::WAVES_N;
+  const int t0 = tb0 + blockIdx.x * C::BN;
+  const int split = blockIdx.y;
+  const int vt0 = split * tiles_per_split;
+  const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
+
+  int tok[C::NB], cur[C::NB], nxt[C::NB];
+  float lse2[C::NB], coef[C::NB], sc[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    tok[nb] = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
+    cur[nb] = K;
+    nxt[nb] = kIdxEnd;
+    lse2[nb] = 0.f;
+    coef[nb] = 0.f;
+    sc[nb] = 0.f;
+    if (tok[nb] < T) {
+      sc[nb] = srow[tok[nb]];
+      coef[nb] = sc[nb] * Mrow[tok[nb]];
+      // rows with zero scale (masked) contribute exact zeros whatever their lse
+      lse2[nb] = sc[nb] != 0.f ? lse[tok[nb]] * kLog2e : INFINITY;
+      const int* row = idx_s + (int64_t)tok[nb] * K;
+      cur[nb] = lower_bound_row(row, K, vb0 + vt0 * C::BM);
+      nxt[nb] = cur[nb] < K ? row[cur[nb]] : kIdxEnd;
+    }
+  }
+
+  Tile<C> tile;
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const int v0 = vb0 + vt * C::BM;
+    tile_mma<C>(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    const int vbase = v0 + wave_m * C::WM;
+    const int vend = min(v0 + C::BM, V);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + mb * 32 + acc_row(r, lane);
+          const float z = tile.acc[mb][nb][r];
+          tile.acc[mb][nb][r] = (v < V) ? coef[nb] * fast_exp2(z * kLog2e - lse2[nb]) : 0.f;
+        }
+      while (nxt[nb] < vend) {
+        const int vl = nxt[nb] - vbase;
+        if (vl >= 0 && vl < C::WM) {
+          const int rr = vl & 31;
+          if (((rr >> 2) & 1) == (lane >> 5)) {
+            const int sel = (vl >> 5) * 16 + (rr >> 3) * 4 + (rr & 3);
+            const float sp = sc[nb] * p_s[(int64_t)tok[nb] * K + cur[nb]];
+#pragma unroll
+            for (int q = 0; q < C::MB * 16; ++q)
+              if (q == sel) tile.acc[q / 16][nb][q % 16] -= sp;
+          }
+        }
+        ++cur[nb];
+        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok[nb] * K + cur[nb]] : kIdxEnd;
+      }
+      // G rows: four consecutive vocabulary entries per register group
+      const int64_t trow = tok[nb] - tb0;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int vcol = vbase - vb0 + mb * 32 + 8 * i + 4 * (lane >> 5);
+          store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
+                      tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
+        }
+      // G^T rows: neighbouring lanes hold neighbouring tokens; swap one value
+      // so that each lane writes a pair of tokens for one vocabulary entry.
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float a0 = tile.acc[mb][nb][r], a1 = tile.acc[mb][nb][r + 1];
+          const float recv = __shfl_xor(odd ? a0 : a1, 1);
+          const int vrow = vbase - vb0 + mb * 32 + acc_row(r, lane);
+          if (!odd) store2<TIn>(Gt + (int64_t)vrow * ldGt + trow, a0, recv);
+          else store2<TIn>(Gt + (int64_t)(vrow + 1) * ldGt + trow - 1, recv, a1);
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------ plain contraction --
+// out[m, n] (+)= sum_k X[m, k] Y[n, k] for m < M, n < N (fp32 out).
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(const typename C::TIn* __restrict__ X, int64_t ldx,
+                                                                 int M, const typename C::TIn* __restrict__ Y,
+                                                                 int64_t ldy, int N, int kdim,
+                                                                 float* __restrict__ out, int64_t ldo, int beta) {
+  using TIn = typename C::TIn;
+  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_m = wave / C::WAVES_N;
+  const int wave_n = wave % C::WAVES_N;
+  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
+  Tile<C> tile;
+  tile_mma<C>(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      const int n = n0 + wave_n * C::WN + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wave_m * C::WM + mb * 32 + acc_row(r, lane);
+        if (m < M && n < N) {
+          float* o = out + (int64_t)m * ldo + n;
+          const float a = tile.acc[mb][nb][r];
+          *o = beta ? *o + a : a;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launchers --
+using CfgBF16 = TileCfg<bf16_t, 128, 128, 64, 64>;
+using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
+
+template <typename TIn>
+struct CfgOf;
+template <>
+struct CfgOf<bf16_t> { using type = CfgBF16; };
+template <>
+struct CfgOf<float> { using type = CfgF32; };
+
+#define CKL_LAUNCH_CHECK() \
+  do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
+
+hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_count_mask(const uint8_t* mask, int T, int* N, hipStream_t st) {
+  hipLaunchKernelGGL(count_mask_kernel, dim3(1), dim3(1024), 0, st, mask, T, N);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const int* N, int T, int Tp, float* s,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(row_scale_kernel, dim3((Tp + 255) / 256), dim3(256), 0, st, mask, grad_loss, N, T, Tp, s);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
+                               float* Erow, float* Mrow, float* zg_s, int* bad, hipStream_t st) {
+  int Kp = 64;
+  while (Kp < K) Kp <<= 1;
+  const size_t lds = (size_t)Kp * 8;
+  hipLaunchKernelGGL(teacher_prep_kernel, dim3(T), dim3(64), lds, st, idx, tlogit, T, K, Kp, V, idx_s, p_s, Erow,
+                     Mrow, zg_s, bad);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+template <typename TIn>
+static hipError_t fwd_lse_t(const void* H, const void* W, int T, int d, int V, int K, const int* idx_s, float* zg_s,
+                            void* part, int n_splits, int tiles_per_split, hipStream_t st) {
+  using C = typename CfgOf<TIn>::type;
+  const int n_vtiles = (V + C::BM - 1) / C::BM;
+  dim3 grid((T + C::BN - 1) / C::BN, n_splits);
+  hipLaunchKernelGGL(fwd_lse_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)H, (const TIn*)W, T, d, V, K,
+                     idx_s, zg_s, (float2*)part, n_vtiles, tiles_per_split);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
+                          float* zg_s, void* part, int n_splits, int tiles_per_split, hipStream_t st) {
+  return in_bf16 ? fwd_lse_t<bf16_t>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, st)
+                 : fwd_lse_t<float>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, st);
+}
+
+hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
+                               const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
+                               float* row_loss, double* blk_sum, const int* N, float* loss, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(256), 0, st, (const float2*)part, S, T, K, p_s, zg_s, Erow,
+                     Mrow, mask, lse, row_loss, blk_sum);
+  CKL_LAUNCH_CHECK();
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, blk_sum, nblk, N, loss);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_transpose_pad(int in_bf16, const void* src, int R, int C, int Rp, void* dst, int64_t ldd,
+                                hipStream_t st) {
+  dim3 grid((Rp + 63) / 64, (C + 63) / 64);
+  if (in_bf16)
+    hipLaunchKernelGGL(transpose_pad_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src, R, C, Rp,
+                       (bf16_t*)dst, ldd);
+  else
+    hipLaunchKernelGGL(transpose_pad_kernel<float>, grid, dim3(256), 0, st, (const float*)src, R, C, Rp, (float*)dst,
+                       ldd);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_f32_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, (bf16_t*)dst, n);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+template <typename TIn>
+static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
+                             const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
+                             int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G,
+                             int64_t ldG, void* Gt, int64_t ldGt, hipStream_t st) {
+  using C = typename CfgOf<TIn>::type;
+  const int n_vtiles = v_rows / C::BM;
+  dim3 grid(t_rows / C::BN, n_splits);
+  hipLaunchKernelGGL(bwd_grad_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)H, (const TIn*)W, T, d, V, K,
+                     idx_s, p_s, Mrow, lse, srow, tb0, vb0, n_vtiles, tiles_per_split, (TIn*)G, ldG, (TIn*)Gt, ldGt);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_grad(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
+                           const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
+                           int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G, int64_t ldG,
+                           void* Gt, int64_t ldGt, hipStream_t st) {
+  return in_bf16 ? bwd_grad_t<bf16_t>(H, W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, t_rows, vb0, v_rows,
+                                      n_splits, tiles_per_split, G, ldG, Gt, ldGt, st)
+                 : bwd_grad_t<float>(H, W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, t_rows, vb0, v_rows,
+                                     n_splits, tiles_per_split, G, ldG, Gt, ldGt, st);
+}
+
+template <typename TIn>
+static hipError_t gemm_store_t(const void* X, int64_t ldx, int M, const void* Y, int64_t ldy, int N, int kdim,
+                               float* out, int64_t ldo, int beta, hipStream_t st) {
+  using C = typename CfgOf<TIn>::type;
+  dim3 grid((M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(gemm_store_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)X, ldx, M, (const TIn*)Y, ldy,
+                     N, kdim, out, ldo, beta);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_store(int in_bf16, const void* X, int64_t ldx, int M, const void* Y, int64_t ldy, int N,
+                             int kdim, float* out, int64_t ldo, int beta, hipStream_t st) {
+  return in_bf16 ? gemm_store_t<bf16_t>(X, ldx, M, Y, ldy, N, kdim, out, ldo, beta, st)
+                 : gemm_store_t<float>(X, ldx, M, Y, ldy, N, kdim, out, ldo, beta, st);
+}
+
+int tile_rows_m() { return CfgBF16::BM; }
+int tile_rows_n() { return CfgBF16::BN; }
+
+}  // namespace ckl

@@ -1,0 +1,144 @@
+/*
+ * ckl.h -- C ABI of libckl, a fused chunked forward-KL distillation loss for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Given student hidden states H[T, d], the output-head
+ * weights W[V, d] and, for every row t, a sparse cached teacher made of K
+ * vocabulary indices idx[t, :] and their logits tlogit[t, :], the library
+ * evaluates the forward KL divergence KL(p_t || q_t) between
+ *   p_t = softmax over the K cached logits (temperature 1), zero elsewhere,
+ *   q_t = softmax(z_t) with z_t = W h_t (full vocabulary),
+ * in the sparse form given in the objective section of the README page
+ * "Chunked KL loss, running Knowledge Distillation locally in less <6GB VRAM":
+ *   l_t = sum_k p_tk log p_tk - sum_k p_tk z_t[idx_tk] + M_t logsumexp(z_t),
+ * with M_t = sum_k p_tk (the teacher mass; 1 for renormalised logits), and
+ *   loss = (1/N) sum_{t : mask_t = 1} l_t,   N = number of unmasked rows.
+ * N = 0 gives loss = 0 and zero gradients.
+ *
+ * The backward pass (the "Full Chunked KL" paragraph of the same page: the
+ * logits are recomputed chunk by chunk and the closed-form gradient is
+ * applied) uses the logit gradient
+ *   G[t, v] = s_t (M_t q_t[v] - p~_t[v]),   s_t = grad_loss * mask_t / N,
+ * where p~_t is p_t scattered to its indices, and returns dH = G W and
+ * dW = G^T H.  The T x V logit tensor is never stored: logit tiles live in
+ * registers, and the backward keeps only a bounded block of G (its size is set
+ * by `chunk`, see below).
+ *
+ * Layouts (all row-major, densely packed, no strides):
+ *   H       [T, d]  in_dtype         W        [V, d]  in_dtype
+ *   idx     [T, K]  int32            tlogit   [T, K]  float32
+ *   mask    [T]     uint8 (nonzero = keep) or NULL (all rows kept)
+ *   lse     [T]     float32          row_loss [T]     float32
+ *   dH      [T, d]  dh_dtype         dW       [V, d]  dw_dtype
+ *   loss, grad_loss: one float32 each.
+ * Every array pointer is a DEVICE pointer (memory of the GPU current when the
+ * call is made); `stream` is a hipStream_t (NULL = the legacy default stream).
+ * Device arrays must be 16-byte aligned.
+ *
+ * Ownership.  The caller allocates every buffer, the workspace included.  The
+ * library allocates no device memory, keeps no state between calls and holds
+ * no pointer after a call returns (apart from work queued on `stream`).
+ *
+ * Execution.  Calls enqueue kernels on `stream` and return without waiting
+ * (no host synchronisation), except when `validate` is set (see below).
+ * Results are bitwise reproducible for identical inputs, problem and
+ * workspace: there are no floating-point atomics.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ * on error nothing is launched and outputs are untouched.  HIP launch errors
+ * return CKL_ERR_HIP.  ckl_last_error() returns a thread-local message that
+ * describes the last non-OK status returned on the calling thread.
+ */
+#ifndef CKL_H_
+#define CKL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CKL_OK = 0,
+  CKL_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad alignment          */
+  CKL_ERR_UNSUPPORTED = 2, /* valid request outside what this build handles  */
+  CKL_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes below ckl_workspace_size()  */
+  CKL_ERR_BAD_INDEX = 4,   /* validate = 1 found idx out of [0, V) or repeated */
+  CKL_ERR_HIP = 5          /* a HIP runtime call failed                      */
+} ckl_status;
+
+typedef enum { CKL_F32 = 0, CKL_BF16 = 1 } ckl_dtype;
+
+typedef struct {
+  int64_t T;      /* rows (batch x sequence, flattened), >= 1              */
+  int64_t d;      /* hidden size, >= 8 and a multiple of 8                 */
+  int64_t V;      /* vocabulary size, >= 1                                 */
+  int64_t K;      /* teacher entries per row, 1 <= K <= min(V, 4096)       */
+  int64_t chunk;  /* backward G-block budget in rows of V entries, >= 1:   */
+                  /* the backward keeps at most about chunk*V logit        */
+                  /* gradients at a time (rounded up to whole tiles).      */
+  int32_t in_dtype;  /* ckl_dtype of H and W                               */
+  int32_t dh_dtype;  /* ckl_dtype of dH                                    */
+  int32_t dw_dtype;  /* ckl_dtype of dW                                    */
+  int32_t validate;  /* 1: check idx on the device (range, no repeats) and */
+                     /* synchronise `stream` to report CKL_ERR_BAD_INDEX.  */
+                     /* 0: no check; idx is a precondition.  Out-of-range  */
+                     /* entries never cause an out-of-bounds access (they  */
+                     /* match no vocabulary column) but the result is then */
+                     /* undefined, as it is for repeated entries.          */
+} ckl_problem;
+
+/* Workspace bytes needed by ckl_forward (which = 0) or ckl_backward
+ * (which = 1) for problem *p.  Writes *bytes; returns CKL_OK or
+ * CKL_ERR_INVALID_ARG / CKL_ERR_UNSUPPORTED for a bad problem. */
+ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes);
+
+/* Forward pass: loss, per-row log-sum-exp and per-row KL.
+ *   H, W, idx, tlogit, mask: inputs as above (mask may be NULL).
+ *   loss:     [1] device float32, the masked mean of l_t.
+ *   lse:      [T] device float32, logsumexp_v z_t[v] for kept rows, 0 for
+ *             masked rows.  ckl_backward takes this array back.
+ *   row_loss: [T] device float32 or NULL; l_t for kept rows, 0 for masked.
+ *   ws:       device workspace of at least ckl_workspace_size(p, 0) bytes;
+ *             its contents on entry do not matter.
+ * The loss and its logit-gradient formula follow the objective section and
+ * the Full Chunked KL paragraph of the README page named above. */
+ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W,
+                       const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                       float* loss, float* lse, float* row_loss,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass: dH and dW of grad_loss * loss.
+ *   lse:       [T] from ckl_forward on the same inputs.
+ *   grad_loss: [1] device float32 or NULL (= 1).
+ *   dH, dW:    outputs, overwritten (not accumulated into).
+ *   ws:        device workspace of at least ckl_workspace_size(p, 1) bytes.
+ * The logit tiles are recomputed and never stored beyond a G block of about
+ * chunk*V entries. */
+ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
+                        const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                        const float* lse, const float* grad_loss,
+                        void* dH, void* dW, void* ws, size_t ws_bytes, void* stream);
+
+/* The G-block plan ckl_backward uses for problem *p: out[0] = Tc (token rows
+ * per block), out[1] = Vc (vocabulary columns per block), out[2] = number of
+ * token blocks, out[3] = number of vocabulary blocks.  dW is read-modified-
+ * written once per extra token block and dH once per extra vocabulary block.
+ * Host-only; touches no device. */
+ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]);
+
+/* Static description of a status code. */
+const char* ckl_status_string(ckl_status s);
+
+/* Thread-local detail of the last non-OK status on this thread ("" if none). */
+const char* ckl_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int32_t ckl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKL_H_ */

@@ -1,0 +1,66 @@
+"""Helpers shared by the GPU tests: run the HIP library on host inputs from
+``synth`` and bring the results back as float64 numpy arrays.  Imports the
+product package only; the oracle is called by the tests themselves."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+# Tolerances (the oracle is fp64; the GPU path computes in fp32 with inputs as
+# given).  bf16 inputs: loss relative error <= 2e-3 and dH / dW max-abs error
+# <= 1e-2 * max|ref|.  fp32 inputs: 1e-5 relative for both.
+TOL = {
+    "bf16": dict(loss_rel=2e-3, grad_rel=1e-2),
+    "f32": dict(loss_rel=1e-5, grad_rel=1e-5),
+}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x, device="cuda"):
+    import torch
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).to(device)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).to(device)
+    else:
+        H = torch.from_numpy(x.H).to(device)
+        W = torch.from_numpy(x.W).to(device)
+    idx = torch.from_numpy(x.idx).to(device)
+    tl = torch.from_numpy(x.tlogit).to(device)
+    mask = None if x.mask is None else torch.from_numpy(x.mask).to(device)
+    return H, W, idx, tl, mask
+
+
+def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False,
+            want_grads=True):
+    """Forward + backward through the C ABI.  Returns float64 numpy results."""
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    H, W, idx, tl, m = to_device(x)
+    if not isinstance(mask, str):
+        m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=np.uint8)).cuda()
+    chunk = x.chunk if chunk is None else chunk
+    loss, lse, row_loss = ckl.forward(H, W, idx, tl, m, chunk=chunk, validate=validate, want_row_loss=True)
+    out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy())
+    if want_grads:
+        g = torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
+        dH, dW = ckl.backward(H, W, idx, tl, m, lse, g, chunk=chunk, dh_dtype=dh_dtype, dw_dtype=dw_dtype,
+                              validate=validate)
+        torch.cuda.synchronize()
+        out["dH"] = dH.double().cpu().numpy()
+        out["dW"] = dW.double().cpu().numpy()
+    del H, W, idx, tl, m
+    torch.cuda.empty_cache()
+    return out
+
+
+def max_rel(got, ref):
+    """max |got - ref| / max |ref| (the gradient criterion)."""
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    return err / scale if scale > 0 else err
