@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked forward-KL loss (forward + backward) on one
+MI355X.
+
+One step = ckl_forward + ckl_backward over one batch of synthetic inputs that
+are resident in HBM before timing starts.  Default workload: T = 32,768 rows,
+d = 2,880, V = 201,088, K = 100 cached teacher entries, chunk = 2,048, bf16 H
+and W (the pages' 32K-context, 201,088-token-vocabulary case).
+
+Prints ONE JSON line with tokens/s, TFLOP/s (8 T V d useful flops per step),
+the fraction of the bf16 dense MFMA peak, peak HBM, a roofline entry for the
+dominant kernel (timed live with HIP events on the launch stream) and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("chunked_kl_loss_amd/csrc/ckl_kernels.hip", "chunked_kl_loss_amd/csrc/ckl_tile.hpp",
+                  "chunked_kl_loss_amd/csrc/ckl_common.hpp", "chunked_kl_loss_amd/csrc/ckl_api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload(x, dev):
+    """Host inputs -> device tensors (bf16 bit patterns are reinterpreted)."""
+    import numpy as np
+    import torch
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        H = torch.from_numpy(x.H).to(dev)
+        W = torch.from_numpy(x.W).to(dev)
+    idx = torch.from_numpy(x.idx).to(dev)
+    tl = torch.from_numpy(x.tlogit).to(dev)
+    mask = None if x.mask is None else torch.from_numpy(x.mask).to(dev)
+    return H, W, idx, tl, mask
+
+
+def cpu_baseline(x, rows: int):
+    """The fp64 oracle, as it stands, on the first `rows` rows of the workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    sl = slice(0, rows)
+    mask = None if x.mask is None else x.mask[sl]
+    t0 = time.perf_counter()
+    r = oracle.kl_dense(x.H[sl], x.W, x.idx[sl], x.tlogit[sl], mask=mask, block=128)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["loss"])
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {x.T} rows of the same workload (full d={x.d}, V={x.V}, K={x.K}); "
+                      f"fp64 dense forward + backward in {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="synthetic workload id (0-4); 2 is the headline")
+    ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU-baseline sample (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the loss shards by rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    from chunked_kl_loss_amd import _binding as B
+    from synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = ckl.load_library()
+    w = WORKLOADS[args.workload]
+    chunk = args.chunk or w.chunk
+    log(f"generating workload {w.name} (seed {args.seed}) ...")
+    t0 = time.perf_counter()
+    x = make_inputs(w, seed=args.seed)
+    log(f"  inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.empty(1, device=dev)  # initialise the context before resetting the peak counter
+    torch.cuda.reset_peak_memory_stats(dev)
+    H, W, idx, tl, mask = upload(x, dev)
+    T, d, V, K = x.T, x.d, x.V, x.K
+    in_code = B.CKL_BF16 if x.dtype == "bf16" else B.CKL_F32
+    prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32)
+    plan = B.backward_plan(prob)
+    ws_f = torch.empty(B.workspace_size(prob, 0), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = ctypes.byref(prob)
+    mp = None if mask is None else mask.data_ptr()
+
+    def fwd():
+        B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, loss.data_ptr(),
+                                lse.data_ptr(), None, ws_f.data_ptr(), ws_f.numel(), sp), lib)
+
+    def bwd():
+        B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, lse.data_ptr(),
+                                 None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(), ws_b.numel(), sp), lib)
+
+    log(f"warmup {args.warmup} steps; backward plan {plan}")
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize(dev)
+    if not np.isfinite(loss.item()):
+        raise RuntimeError("non-finite loss")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ckl.timing_enable(True)
+    torch.cuda.synchronize(dev)
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t_start
+    ckl.timing_enable(False)
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = wall * 1e3 / args.steps
+    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+    log(f"timed {args.steps} steps: {step_ms:.2f} ms/step (fwd {np.mean(fwd_ms):.2f}, bwd {np.mean(bwd_ms):.2f})")
+
+    # ---- per-kernel timing and roofline of the dominant kernel
+    kt = ckl.timing_read()
+    flops_step = 8.0 * T * V * d
+    algo_flops = {"fwd_lse": 2.0 * T * V * d, "bwd_grad": 2.0 * T * V * d, "gemm_dh": 2.0 * T * V * d,
+                  "gemm_dw": 2.0 * T * V * d}
+    kernels = {k: {"total_ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                   "avg_launch_ms": (ms / n if n else 0.0)} for k, (ms, n) in kt.items()}
+    dom = max(algo_flops, key=lambda k: kt[k][0])
+    dom_ms, dom_n = kt[dom]
+    achieved = algo_flops[dom] * args.steps / (dom_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        ent = tr.get("kernels", {}).get(dom)
+        if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
+            traffic = ent["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic,
+                "avg_launch_ms": dom_ms / dom_n, "launches_per_step": dom_n / args.steps,
+                "algorithmic_flops_per_step": algo_flops[dom]}
+
+    tokens_s = T / (step_ms * 1e-3)
+    tflops = flops_step / (step_ms * 1e-3) / 1e12
+    n_valid = int(T if x.mask is None else x.mask.sum())
+    result = {
+        "metric": "fused KL fwd+bwd tokens/s and TFLOP/s (% MFMA bf16 peak); peak HBM GiB",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generator: H~N(0,1), W~N(0,1/d), K distinct uniform teacher indices, "
+                "teacher logits N(0,2) sorted)",
+        "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "chunk": chunk,
+                   "masked_rows": T - n_valid, "parallelism": "single GPU",
+                   "backward_plan": plan},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "peak_hbm_gib": peak_gib,
+        "fwd_ms": float(np.mean(fwd_ms)),
+        "bwd_ms": float(np.mean(bwd_ms)),
+        "fwd_ms_min": float(np.min(fwd_ms)),
+        "bwd_ms_min": float(np.min(bwd_ms)),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    del H, W, idx, tl, mask, ws_f, ws_b, dH, dW
+    torch.cuda.empty_cache()
+    if args.cpu_rows > 0:
+        log(f"oracle CPU baseline on {args.cpu_rows} rows ...")
+        result["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, x.T))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

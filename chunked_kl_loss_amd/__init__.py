@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     forward,
     load_library,
     make_problem,
+    timing_enable,
+    timing_read,
     workspace_size,
 )
 from .autograd import ChunkedKLLoss, chunked_kl_loss  # noqa: F401

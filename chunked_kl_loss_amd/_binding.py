@@ -26,6 +26,8 @@ EXPORTED = (
     "ckl_forward",
     "ckl_backward",
     "ckl_backward_plan",
+    "ckl_timing_enable",
+    "ckl_timing_read",
     "ckl_status_string",
     "ckl_last_error",
     "ckl_version",
@@ -75,6 +77,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckl_backward.restype = i32
     lib.ckl_backward_plan.argtypes = [P, i64p]
     lib.ckl_backward_plan.restype = i32
+    lib.ckl_timing_enable.argtypes = [ctypes.c_int]
+    lib.ckl_timing_enable.restype = i32
+    lib.ckl_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), i64p]
+    lib.ckl_timing_read.restype = i32
     lib.ckl_status_string.argtypes = [i32]
     lib.ckl_status_string.restype = ctypes.c_char_p
     lib.ckl_last_error.argtypes = []
@@ -109,6 +115,27 @@ def backward_plan(prob: Problem):
     out = (ctypes.c_int64 * 4)()
     check(lib.ckl_backward_plan(ctypes.byref(prob), out), lib)
     return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3])
+
+
+KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dh", "gemm_dw", "transpose",
+                  "other")
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (and clear) or stop the library's per-kernel event timing."""
+    lib = load_library()
+    check(lib.ckl_timing_enable(int(bool(on))), lib)
+
+
+def timing_read() -> dict:
+    """{class name: (total ms, launches)} accumulated since timing_enable()."""
+    lib = load_library()
+    out = {}
+    for i, name in enumerate(KERNEL_CLASSES):
+        ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+        check(lib.ckl_timing_read(i, ctypes.byref(ms), ctypes.byref(n)), lib)
+        out[name] = (ms.value, n.value)
+    return out
 
 
 # ------------------------------------------------------------ torch layer --

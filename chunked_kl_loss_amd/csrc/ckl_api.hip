@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/ckl.h"
 #include "ckl_kernels.hpp"
@@ -39,6 +41,56 @@ ckl_status hip_fail(hipError_t e, const char* what) {
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 constexpr int kTargetWorkgroups = 2048;  // fused kernels: row blocks x vocabulary splits
+
+// ------------------------------------------------------------------ timing --
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int cls; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  double total_ms[CKL_KERNEL_CLASSES] = {};
+  int64_t launches[CKL_KERNEL_CLASSES] = {};
+};
+TimingState g_timing;
+
+// Launch `fn` (returning hipError_t), bracketed by timing events when enabled.
+template <class Fn>
+hipError_t timed(int cls, hipStream_t st, Fn&& fn) {
+  if (!g_timing.on) return fn();
+  std::pair<hipEvent_t, hipEvent_t> ev{};
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.pool.empty()) { ev = g_timing.pool.back(); g_timing.pool.pop_back(); }
+  }
+  hipError_t e;
+  if (!ev.first) {
+    if ((e = hipEventCreate(&ev.first)) != hipSuccess) return e;
+    if ((e = hipEventCreate(&ev.second)) != hipSuccess) return e;
+  }
+  if ((e = hipEventRecord(ev.first, st)) != hipSuccess) return e;
+  if ((e = fn()) != hipSuccess) return e;
+  if ((e = hipEventRecord(ev.second, st)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.pending.push_back({cls, ev.first, ev.second});
+  return hipSuccess;
+}
+
+hipError_t timing_drain() {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return e;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return e;
+    g_timing.total_ms[r.cls] += ms;
+    g_timing.launches[r.cls] += 1;
+    g_timing.pool.push_back({r.a, r.b});
+  }
+  g_timing.pending.clear();
+  return hipSuccess;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -210,18 +262,29 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   int* bad = (int*)(b + w.bad);
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
 
-  HIP_TRY(ckl::launch_count_mask(mask, T, N, st), "count_mask");
-  if (p->validate) HIP_TRY(ckl::launch_fill_i32(bad, 1, 0, st), "fill");
-  HIP_TRY(ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s, p->validate ? bad : nullptr, st),
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
+  HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
+                [&] {
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
+                                                  p->validate ? bad : nullptr, st);
+                }),
           "teacher_prep");
   if (p->validate) {
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits, (int)q.f_tps, st),
+  HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
+                [&] {
+                  return ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits,
+                                             (int)q.f_tps, st);
+                }),
           "fwd_lse");
-  HIP_TRY(ckl::launch_fwd_finalize(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, E, M, mask, lse, row_loss,
-                                   (double*)(b + w.blk), N, loss, st),
+  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                [&] {
+                  return ckl::launch_fwd_finalize(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, E, M, mask, lse,
+                                                  row_loss, (double*)(b + w.blk), N, loss, st);
+                }),
           "fwd_finalize");
   return CKL_OK;
 }
@@ -257,18 +320,26 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
 
-  HIP_TRY(ckl::launch_count_mask(mask, T, N, st), "count_mask");
-  if (p->validate) HIP_TRY(ckl::launch_fill_i32(bad, 1, 0, st), "fill");
-  HIP_TRY(ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, nullptr, M, nullptr, p->validate ? bad : nullptr,
-                                   st),
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
+  HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
+                [&] {
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, nullptr, M, nullptr,
+                                                  p->validate ? bad : nullptr, st);
+                }),
           "teacher_prep");
   if (p->validate) {
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st), "row_scale");
-  HIP_TRY(ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp, st), "transpose H");
-  HIP_TRY(ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp, st), "transpose W");
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st); }),
+          "row_scale");
+  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp, st); }),
+          "transpose H");
+  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp, st); }),
+          "transpose W");
 
   const char* Htb = (const char*)Ht;
   const char* Wtb = (const char*)Wt;
@@ -280,21 +351,37 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
       const int64_t trows = std::min(q.Tc, q.Tp - tb0);
       int64_t splits, tps;
       pick_splits(trows / q.BN, vrows / q.BM, &splits, &tps);
-      HIP_TRY(ckl::launch_bwd_grad(q.in_bf16, H, W, T, d, V, K, idx_s, p_s, M, lse, srow, (int)tb0, (int)trows,
-                                   (int)vb0, (int)vrows, (int)splits, (int)tps, G, vrows, Gt, trows, st),
+      HIP_TRY(timed(CKL_KERNEL_BWD_GRAD, st,
+                    [&] {
+                      return ckl::launch_bwd_grad(q.in_bf16, H, W, T, d, V, K, idx_s, p_s, M, lse, srow, (int)tb0,
+                                                  (int)trows, (int)vb0, (int)vrows, (int)splits, (int)tps, G, vrows,
+                                                  Gt, trows, st);
+                    }),
               "bwd_grad");
       // dH[tb0 .. tb0 + trows) (+)= G W[vb0 .. vb0 + vrows)
-      HIP_TRY(ckl::launch_gemm_store(q.in_bf16, G, vrows, (int)std::min(trows, q.T - tb0), Wtb + vb0 * q.esz, q.Vp, d,
-                                     (int)vrows, dHacc + tb0 * q.d, q.d, vb > 0, st),
+      HIP_TRY(timed(CKL_KERNEL_GEMM_DH, st,
+                    [&] {
+                      return ckl::launch_gemm_store(q.in_bf16, G, vrows, (int)std::min(trows, q.T - tb0),
+                                                    Wtb + vb0 * q.esz, q.Vp, d, (int)vrows, dHacc + tb0 * q.d, q.d,
+                                                    vb > 0, st);
+                    }),
               "gemm dH");
       // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)
-      HIP_TRY(ckl::launch_gemm_store(q.in_bf16, Gt, trows, (int)std::min(vrows, q.V - vb0), Htb + tb0 * q.esz, q.Tp,
-                                     d, (int)trows, dWacc + vb0 * q.d, q.d, tb > 0, st),
+      HIP_TRY(timed(CKL_KERNEL_GEMM_DW, st,
+                    [&] {
+                      return ckl::launch_gemm_store(q.in_bf16, Gt, trows, (int)std::min(vrows, q.V - vb0),
+                                                    Htb + tb0 * q.esz, q.Tp, d, (int)trows, dWacc + vb0 * q.d, q.d,
+                                                    tb > 0, st);
+                    }),
               "gemm dW");
     }
   }
-  if (p->dh_dtype == CKL_BF16) HIP_TRY(ckl::launch_cast_f32_bf16(dHacc, dH, q.T * q.d, st), "cast dH");
-  if (p->dw_dtype == CKL_BF16) HIP_TRY(ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st), "cast dW");
+  if (p->dh_dtype == CKL_BF16)
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dHacc, dH, q.T * q.d, st); }),
+            "cast dH");
+  if (p->dw_dtype == CKL_BF16)
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),
+            "cast dW");
   return CKL_OK;
 }
 
@@ -307,6 +394,29 @@ ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]) {
   out[1] = q.Vc;
   out[2] = q.nT;
   out[3] = q.nV;
+  return CKL_OK;
+}
+
+ckl_status ckl_timing_enable(int on) {
+  if (on != 0 && on != 1) return fail(CKL_ERR_INVALID_ARG, "on must be 0 or 1");
+  if (on) {
+    hipError_t e = timing_drain();
+    if (e != hipSuccess) return hip_fail(e, "draining timing events");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    for (int i = 0; i < CKL_KERNEL_CLASSES; ++i) { g_timing.total_ms[i] = 0.0; g_timing.launches[i] = 0; }
+  }
+  g_timing.on = on != 0;
+  return CKL_OK;
+}
+
+ckl_status ckl_timing_read(int kernel_class, double* total_ms, int64_t* launches) {
+  if (kernel_class < 0 || kernel_class >= CKL_KERNEL_CLASSES) return fail(CKL_ERR_INVALID_ARG, "bad kernel class");
+  if (!total_ms || !launches) return fail(CKL_ERR_INVALID_ARG, "output pointer is NULL");
+  hipError_t e = timing_drain();
+  if (e != hipSuccess) return hip_fail(e, "reading timing events");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  *total_ms = g_timing.total_ms[kernel_class];
+  *launches = g_timing.launches[kernel_class];
   return CKL_OK;
 }
 

@@ -36,8 +36,9 @@
  * Device arrays must be 16-byte aligned.
  *
  * Ownership.  The caller allocates every buffer, the workspace included.  The
- * library allocates no device memory, keeps no state between calls and holds
- * no pointer after a call returns (apart from work queued on `stream`).
+ * library allocates no device memory, keeps no state between calls (apart from
+ * the optional timing records, see ckl_timing_enable) and holds no pointer
+ * after a call returns (apart from work queued on `stream`).
  *
  * Execution.  Calls enqueue kernels on `stream` and return without waiting
  * (no host synchronisation), except when `validate` is set (see below).
@@ -127,6 +128,31 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
  * written once per extra token block and dH once per extra vocabulary block.
  * Host-only; touches no device. */
 ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]);
+
+/* Kernel classes for the timing records below. */
+typedef enum {
+  CKL_KERNEL_TEACHER_PREP = 0, /* teacher softmax + sort                      */
+  CKL_KERNEL_FWD_LSE = 1,      /* forward logit tiles + online LSE + gather    */
+  CKL_KERNEL_FWD_FINALIZE = 2, /* split merge, row loss, masked mean          */
+  CKL_KERNEL_BWD_GRAD = 3,     /* backward logit recompute + G epilogue       */
+  CKL_KERNEL_GEMM_DH = 4,      /* dH (+)= G W                                 */
+  CKL_KERNEL_GEMM_DW = 5,      /* dW (+)= G^T H                               */
+  CKL_KERNEL_TRANSPOSE = 6,    /* H^T and W^T staging                         */
+  CKL_KERNEL_OTHER = 7,        /* counts, scales, fills, casts               */
+  CKL_KERNEL_CLASSES = 8
+} ckl_kernel_class;
+
+/* Optional per-kernel timing, a measurement aid.  While enabled (on = 1),
+ * every kernel the library launches is bracketed by two hipEvents recorded on
+ * the launch stream; enabling (again) clears the accumulated records, on = 0
+ * stops recording.  Process-wide; the records are the only state the library
+ * keeps between calls, and the events are its only allocations. */
+ckl_status ckl_timing_enable(int on);
+
+/* Waits for the recorded events, adds their durations to the totals of each
+ * class and returns, for class `kernel_class`, the summed duration in
+ * milliseconds and the number of launches since timing was enabled. */
+ckl_status ckl_timing_read(int kernel_class, double* total_ms, int64_t* launches);
 
 /* Static description of a status code. */
 const char* ckl_status_string(ckl_status s);
