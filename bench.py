@@ -180,8 +180,7 @@ def main():
     # ---- per-kernel timing and roofline of the dominant kernel
     kt = ckl.timing_read()
     flops_step = 8.0 * T * V * d
-    algo_flops = {"fwd_lse": 2.0 * T * V * d, "bwd_grad": 2.0 * T * V * d, "gemm_dh": 2.0 * T * V * d,
-                  "gemm_dw": 2.0 * T * V * d}
+    algo_flops = {"fwd_lse": 2.0 * T * V * d, "bwd_grad": 2.0 * T * V * d, "gemm_dhdw": 4.0 * T * V * d}
     kernels = {k: {"total_ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
                    "avg_launch_ms": (ms / n if n else 0.0)} for k, (ms, n) in kt.items()}
     dom = max(algo_flops, key=lambda k: kt[k][0])

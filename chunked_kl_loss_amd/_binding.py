@@ -117,7 +117,7 @@ def backward_plan(prob: Problem):
     return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3])
 
 
-KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dh", "gemm_dw", "transpose",
+KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dhdw", "reserved5", "transpose",
                   "other")
 
 

@@ -139,8 +139,8 @@ Plan make_plan(const ckl_problem* p) {
   q.T = p->T; q.d = p->d; q.V = p->V; q.K = p->K;
   q.in_bf16 = p->in_dtype == CKL_BF16;
   q.esz = q.in_bf16 ? 2 : 4;
-  q.BM = ckl::tile_rows_m();
-  q.BN = ckl::tile_rows_n();
+  q.BM = ckl::tile_rows_m(q.in_bf16);
+  q.BN = ckl::tile_rows_n(q.in_bf16);
   q.Tp = round_up(q.T, q.BN);
   q.Vp = round_up(q.V, q.BM);
   pick_splits(ceil_div(q.T, q.BN), ceil_div(q.V, q.BM), &q.f_splits, &q.f_tps);
@@ -358,22 +358,14 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
                                                   Gt, trows, st);
                     }),
               "bwd_grad");
+      // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)  (longer k: scheduled first)
       // dH[tb0 .. tb0 + trows) (+)= G W[vb0 .. vb0 + vrows)
-      HIP_TRY(timed(CKL_KERNEL_GEMM_DH, st,
-                    [&] {
-                      return ckl::launch_gemm_store(q.in_bf16, G, vrows, (int)std::min(trows, q.T - tb0),
-                                                    Wtb + vb0 * q.esz, q.Vp, d, (int)vrows, dHacc + tb0 * q.d, q.d,
-                                                    vb > 0, st);
-                    }),
-              "gemm dH");
-      // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)
-      HIP_TRY(timed(CKL_KERNEL_GEMM_DW, st,
-                    [&] {
-                      return ckl::launch_gemm_store(q.in_bf16, Gt, trows, (int)std::min(vrows, q.V - vb0),
-                                                    Htb + tb0 * q.esz, q.Tp, d, (int)trows, dWacc + vb0 * q.d, q.d,
-                                                    tb > 0, st);
-                    }),
-              "gemm dW");
+      const ckl::GemmArgs gdw{Gt, trows, Htb + tb0 * q.esz, q.Tp, dWacc + vb0 * q.d, q.d,
+                              (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
+      const ckl::GemmArgs gdh{G, vrows, Wtb + vb0 * q.esz, q.Vp, dHacc + tb0 * q.d, q.d,
+                              (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
+      HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdw, gdh, st); }),
+              "gemm dW + dH");
     }
   }
   if (p->dh_dtype == CKL_BF16)

@@ -181,22 +181,26 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
 }
 
 // ------------------------------------------------------------ forward LSE --
-// grid.x: token blocks of BN rows; grid.y: vocabulary splits of
-// tiles_per_split tiles of BM rows.  Output part[split * T + t] = (m, s):
-// the base-2 log-sum-exp state of row t over the split.
+// One workgroup per (token block of BN rows, vocabulary split of
+// tiles_per_split tiles of BM rows), n_tblocks x n_splits in all, laid out
+// XCD-aware (kGroupT token blocks per group).  Output part[split * T + t] =
+// (m, s): the base-2 log-sum-exp state of row t over the split.
+constexpr int kGroupT = 8;
+
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
     const int* __restrict__ idx_s, float* __restrict__ zg_s, float2* __restrict__ part, int n_vtiles,
-    int tiles_per_split) {
+    int tiles_per_split, int n_tblocks, int n_splits) {
   using TIn = typename C::TIn;
-  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
-  const int t0 = blockIdx.x * C::BN;
-  const int split = blockIdx.y;
+  int tblock, split;
+  grouped_mn(xcd_remap(blockIdx.x, n_tblocks * n_splits), n_tblocks, n_splits, kGroupT, tblock, split);
+  const int t0 = tblock * C::BN;
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
 
@@ -216,10 +220,10 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     }
   }
 
-  Tile<C> tile;
+  typename C::TileT tile;
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vt * C::BM;
-    tile_mma<C>(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    run_mma(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
 #pragma unroll
@@ -380,8 +384,9 @@ __global__ void cast_f32_bf16_kernel(const float* __restrict__ src, bf16_t* __re
 }
 
 // ------------------------------------------------------------ backward G --
-// Recomputes the logit tiles of the G block rows [tb0, tb0 + 128 gridDim.x),
-// vocabulary [vb0, vb0 + BM n_vtiles) and writes
+// Recomputes the logit tiles of the G block rows [tb0, tb0 + BN n_tblocks),
+// vocabulary [vb0, vb0 + BM n_vtiles) (same workgroup layout as the forward)
+// and writes
 //   G [t - tb0][v - vb0]  (row stride ldG)  and  Gt[v - vb0][t - tb0] (ldGt)
 // with G = s_t (M_t q_t[v] - p~_t[v]); rows t >= T and columns v >= V get 0.
 template <class C>
@@ -389,55 +394,60 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
     const int* __restrict__ idx_s, const float* __restrict__ p_s, const float* __restrict__ Mrow,
     const float* __restrict__ lse, const float* __restrict__ srow, int tb0, int vb0, int n_vtiles,
-    int tiles_per_split, typename C::TIn* __restrict__ G, int64_t ldG, typename C::TIn* __restrict__ Gt,
-    int64_t ldGt) {
+    int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
+    typename C::TIn* __restrict__ Gt, int64_t ldGt) {
   using TIn = typename C::TIn;
-  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
-  const int t0 = tb0 + blockIdx.x * C::BN;
-  const int split = blockIdx.y;
+  int tblock, split;
+  grouped_mn(xcd_remap(blockIdx.x, n_tblocks * n_splits), n_tblocks, n_splits, kGroupT, tblock, split);
+  const int t0 = tb0 + tblock * C::BN;
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
 
-  int tok[C::NB], cur[C::NB], nxt[C::NB];
-  float lse2[C::NB], coef[C::NB], sc[C::NB];
+  // Per-lane token state kept across tiles: only the teacher cursor.  The
+  // per-row scale, mass and LSE are re-read for every tile (cached loads),
+  // which keeps registers free for the accumulators.
+  int cur[C::NB], nxt[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    tok[nb] = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
+    const int tok = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
     cur[nb] = K;
     nxt[nb] = kIdxEnd;
-    lse2[nb] = 0.f;
-    coef[nb] = 0.f;
-    sc[nb] = 0.f;
-    if (tok[nb] < T) {
-      sc[nb] = srow[tok[nb]];
-      coef[nb] = sc[nb] * Mrow[tok[nb]];
-      // rows with zero scale (masked) contribute exact zeros whatever their lse
-      lse2[nb] = sc[nb] != 0.f ? lse[tok[nb]] * kLog2e : INFINITY;
-      const int* row = idx_s + (int64_t)tok[nb] * K;
+    if (tok < T) {
+      const int* row = idx_s + (int64_t)tok * K;
       cur[nb] = lower_bound_row(row, K, vb0 + vt0 * C::BM);
       nxt[nb] = cur[nb] < K ? row[cur[nb]] : kIdxEnd;
     }
   }
 
-  Tile<C> tile;
+  typename C::TileT tile;
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vb0 + vt * C::BM;
-    tile_mma<C>(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    run_mma(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
+      const int tok = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
+      float sc = 0.f, coef = 0.f, lse2 = INFINITY;
+      if (tok < T) {
+        sc = srow[tok];
+        coef = sc * Mrow[tok];
+        // rows with zero scale (masked) give exact zeros whatever their lse
+        if (sc != 0.f) lse2 = lse[tok] * kLog2e;
+      }
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int v = vbase + mb * 32 + acc_row(r, lane);
           const float z = tile.acc[mb][nb][r];
-          tile.acc[mb][nb][r] = (v < V) ? coef[nb] * fast_exp2(z * kLog2e - lse2[nb]) : 0.f;
+          const float g = coef * fast_exp2(z * kLog2e - lse2);
+          tile.acc[mb][nb][r] = (v < V && tok < T) ? g : 0.f;
         }
       while (nxt[nb] < vend) {
         const int vl = nxt[nb] - vbase;
@@ -445,17 +455,17 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
           const int rr = vl & 31;
           if (((rr >> 2) & 1) == (lane >> 5)) {
             const int sel = (vl >> 5) * 16 + (rr >> 3) * 4 + (rr & 3);
-            const float sp = sc[nb] * p_s[(int64_t)tok[nb] * K + cur[nb]];
+            const float sp = sc * p_s[(int64_t)tok * K + cur[nb]];
 #pragma unroll
             for (int q = 0; q < C::MB * 16; ++q)
               if (q == sel) tile.acc[q / 16][nb][q % 16] -= sp;
           }
         }
         ++cur[nb];
-        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok[nb] * K + cur[nb]] : kIdxEnd;
+        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok * K + cur[nb]] : kIdxEnd;
       }
       // G rows: four consecutive vocabulary entries per register group
-      const int64_t trow = tok[nb] - tb0;
+      const int64_t trow = tok - tb0;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -482,21 +492,48 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
 }
 
 // ------------------------------------------------------ plain contraction --
-// out[m, n] (+)= sum_k X[m, k] Y[n, k] for m < M, n < N (fp32 out).
+// out[m, n] (+)= sum_k X[m, k] Y[n, k] for m < M, n < N (fp32 out).  Two
+// independent problems share one launch (the dH and dW products of a G
+// block): workgroups [0, p0.tiles) take problem 0, the rest problem 1, so the
+// tail of one fills the machine with tiles of the other.
+template <typename TIn>
+struct GemmProblem {
+  const TIn* X;
+  int64_t ldx;
+  const TIn* Y;
+  int64_t ldy;
+  float* out;
+  int64_t ldo;
+  int M, N, kdim, beta;
+  int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN)
+};
+
+constexpr int kGroupM = 4;
+
 template <class C>
-__global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(const typename C::TIn* __restrict__ X, int64_t ldx,
-                                                                 int M, const typename C::TIn* __restrict__ Y,
-                                                                 int64_t ldy, int N, int kdim,
-                                                                 float* __restrict__ out, int64_t ldo, int beta) {
-  using TIn = typename C::TIn;
-  __shared__ __attribute__((aligned(16))) TIn smem[C::LDS_BYTES / sizeof(TIn)];
+__global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typename C::TIn> p0,
+                                                                 GemmProblem<typename C::TIn> p1) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
-  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
-  Tile<C> tile;
-  tile_mma<C>(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+  int bid = xcd_remap(blockIdx.x, p0.tiles + p1.tiles);
+  const bool second = bid >= p0.tiles;  // workgroup-uniform
+  if (second) bid -= p0.tiles;
+  // field-wise selection keeps the by-value kernel arguments in registers
+  const typename C::TIn* X = second ? p1.X : p0.X;
+  const typename C::TIn* Y = second ? p1.Y : p0.Y;
+  float* out = second ? p1.out : p0.out;
+  const int64_t ldx = second ? p1.ldx : p0.ldx, ldy = second ? p1.ldy : p0.ldy, ldo = second ? p1.ldo : p0.ldo;
+  const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, kdim = second ? p1.kdim : p0.kdim;
+  const int beta = second ? p1.beta : p0.beta;
+  const int tiles_m = second ? p1.tiles_m : p0.tiles_m, tiles = second ? p1.tiles : p0.tiles;
+  int tm, tn;
+  grouped_mn(bid, tiles_m, tiles / tiles_m, kGroupM, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  typename C::TileT tile;
+  run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -515,15 +552,21 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(const typename 
 }
 
 // ---------------------------------------------------------------- launchers --
-using CfgBF16 = TileCfg<bf16_t, 128, 128, 64, 64>;
+// bf16: 256 x 256 tiles.  The fused logit kernels (heavy per-tile epilogues)
+// run 8 waves (2 per SIMD, so one wave's epilogue overlaps the other's
+// MFMAs); the plain dH / dW contraction runs the software-pipelined 4-wave
+// loop.  fp32 (small problems): 128 x 128 tiles, register-staged loads.
+using CfgBF16 = DmaCfg<256, 256, 128, 64, 4>;
+using CfgBF16Gemm = DmaCfg<256, 256, 128, 128, 4>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
 template <typename TIn>
 struct CfgOf;
 template <>
-struct CfgOf<bf16_t> { using type = CfgBF16; };
+struct CfgOf<bf16_t> { using type = CfgBF16; using gemm = CfgBF16Gemm; };
 template <>
-struct CfgOf<float> { using type = CfgF32; };
+struct CfgOf<float> { using type = CfgF32; using gemm = CfgF32; };
+static_assert(CfgBF16::BM == CfgBF16Gemm::BM && CfgBF16::BN == CfgBF16Gemm::BN, "one tile size per dtype");
 
 #define CKL_LAUNCH_CHECK() \
   do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
@@ -571,9 +614,10 @@ static hipError_t fwd_lse_t(const void* H, const void* W, int T, int d, int V, i
                             void* part, int n_splits, int tiles_per_split, hipStream_t st) {
   using C = typename CfgOf<TIn>::type;
   const int n_vtiles = (V + C::BM - 1) / C::BM;
-  dim3 grid((T + C::BN - 1) / C::BN, n_splits);
-  hipLaunchKernelGGL(fwd_lse_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)H, (const TIn*)W, T, d, V, K,
-                     idx_s, zg_s, (float2*)part, n_vtiles, tiles_per_split);
+  const int n_tblocks = (T + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL(fwd_lse_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,
+                     (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles, tiles_per_split, n_tblocks,
+                     n_splits);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -623,9 +667,10 @@ static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, 
                              int64_t ldG, void* Gt, int64_t ldGt, hipStream_t st) {
   using C = typename CfgOf<TIn>::type;
   const int n_vtiles = v_rows / C::BM;
-  dim3 grid(t_rows / C::BN, n_splits);
-  hipLaunchKernelGGL(bwd_grad_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)H, (const TIn*)W, T, d, V, K,
-                     idx_s, p_s, Mrow, lse, srow, tb0, vb0, n_vtiles, tiles_per_split, (TIn*)G, ldG, (TIn*)Gt, ldGt);
+  const int n_tblocks = t_rows / C::BN;
+  hipLaunchKernelGGL(bwd_grad_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,
+                     (const TIn*)W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, vb0, n_vtiles, tiles_per_split,
+                     n_tblocks, n_splits, (TIn*)G, ldG, (TIn*)Gt, ldGt);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -641,23 +686,36 @@ hipError_t launch_bwd_grad(int in_bf16, const void* H, const void* W, int T, int
 }
 
 template <typename TIn>
-static hipError_t gemm_store_t(const void* X, int64_t ldx, int M, const void* Y, int64_t ldy, int N, int kdim,
-                               float* out, int64_t ldo, int beta, hipStream_t st) {
-  using C = typename CfgOf<TIn>::type;
-  dim3 grid((M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL(gemm_store_kernel<C>, grid, dim3(C::NTHREADS), 0, st, (const TIn*)X, ldx, M, (const TIn*)Y, ldy,
-                     N, kdim, out, ldo, beta);
+static hipError_t gemm_pair_t(const GemmArgs& a0, const GemmArgs& a1, hipStream_t st) {
+  using C = typename CfgOf<TIn>::gemm;
+  GemmProblem<TIn> p[2];
+  const GemmArgs* a[2] = {&a0, &a1};
+  for (int i = 0; i < 2; ++i) {
+    p[i].X = (const TIn*)a[i]->X;
+    p[i].ldx = a[i]->ldx;
+    p[i].Y = (const TIn*)a[i]->Y;
+    p[i].ldy = a[i]->ldy;
+    p[i].out = a[i]->out;
+    p[i].ldo = a[i]->ldo;
+    p[i].M = a[i]->M;
+    p[i].N = a[i]->N;
+    p[i].kdim = a[i]->kdim;
+    p[i].beta = a[i]->beta;
+    p[i].tiles_m = a[i]->M > 0 ? (a[i]->M + C::BM - 1) / C::BM : 0;
+    p[i].tiles = a[i]->M > 0 && a[i]->N > 0 ? p[i].tiles_m * ((a[i]->N + C::BN - 1) / C::BN) : 0;
+  }
+  const int n = p[0].tiles + p[1].tiles;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_store_kernel<C>, dim3(n), dim3(C::NTHREADS), 0, st, p[0], p[1]);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
-hipError_t launch_gemm_store(int in_bf16, const void* X, int64_t ldx, int M, const void* Y, int64_t ldy, int N,
-                             int kdim, float* out, int64_t ldo, int beta, hipStream_t st) {
-  return in_bf16 ? gemm_store_t<bf16_t>(X, ldx, M, Y, ldy, N, kdim, out, ldo, beta, st)
-                 : gemm_store_t<float>(X, ldx, M, Y, ldy, N, kdim, out, ldo, beta, st);
+hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1, hipStream_t st) {
+  return in_bf16 ? gemm_pair_t<bf16_t>(a0, a1, st) : gemm_pair_t<float>(a0, a1, st);
 }
 
-int tile_rows_m() { return CfgBF16::BM; }
-int tile_rows_n() { return CfgBF16::BN; }
+int tile_rows_m(int in_bf16) { return in_bf16 ? CfgBF16::BM : CfgF32::BM; }
+int tile_rows_n(int in_bf16) { return in_bf16 ? CfgBF16::BN : CfgF32::BN; }
 
 }  // namespace ckl

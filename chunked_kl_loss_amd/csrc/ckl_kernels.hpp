@@ -25,11 +25,21 @@ hipError_t launch_bwd_grad(int in_bf16, const void* H, const void* W, int T, int
                            const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
                            int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G, int64_t ldG,
                            void* Gt, int64_t ldGt, hipStream_t st);
-hipError_t launch_gemm_store(int in_bf16, const void* X, int64_t ldx, int M, const void* Y, int64_t ldy, int N,
-                             int kdim, float* out, int64_t ldo, int beta, hipStream_t st);
+// out[m, n] (+)= sum_k X[m, k] Y[n, k]; row-major operands contiguous in k.
+struct GemmArgs {
+  const void* X;
+  int64_t ldx;
+  const void* Y;
+  int64_t ldy;
+  float* out;
+  int64_t ldo;
+  int M, N, kdim, beta;
+};
+// Two independent products in one launch (problem 0's tiles are scheduled first).
+hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1, hipStream_t st);
 
 // Tile extents of the contraction kernels: G blocks are whole tiles.
-int tile_rows_m();  // vocabulary rows per logit tile (BM)
-int tile_rows_n();  // token rows per logit tile (BN)
+int tile_rows_m(int in_bf16);  // vocabulary rows per logit tile (BM)
+int tile_rows_n(int in_bf16);  // token rows per logit tile (BN)
 
 }  // namespace ckl

@@ -135,8 +135,8 @@ typedef enum {
   CKL_KERNEL_FWD_LSE = 1,      /* forward logit tiles + online LSE + gather    */
   CKL_KERNEL_FWD_FINALIZE = 2, /* split merge, row loss, masked mean          */
   CKL_KERNEL_BWD_GRAD = 3,     /* backward logit recompute + G epilogue       */
-  CKL_KERNEL_GEMM_DH = 4,      /* dH (+)= G W                                 */
-  CKL_KERNEL_GEMM_DW = 5,      /* dW (+)= G^T H                               */
+  CKL_KERNEL_GEMM_DHDW = 4,    /* dW (+)= G^T H and dH (+)= G W, one launch   */
+  CKL_KERNEL_RESERVED5 = 5,    /* unused                                      */
   CKL_KERNEL_TRANSPOSE = 6,    /* H^T and W^T staging                         */
   CKL_KERNEL_OTHER = 7,        /* counts, scales, fills, casts               */
   CKL_KERNEL_CLASSES = 8

@@ -72,7 +72,7 @@ def test_workspace_query_and_plan(lib):
     with pytest.raises(B.CklError):
         B.workspace_size(p, 2)
     plan = B.backward_plan(p)
-    assert plan["Tc"] % 128 == 0 and plan["Vc"] % 128 == 0
+    assert plan["Tc"] % 128 == 0 and plan["Vc"] % 128 == 0  # fp32 tiles are 128 x 128
     assert plan["nT"] * plan["Tc"] >= 256 and plan["nV"] * plan["Vc"] >= 2048
 
 
@@ -121,5 +121,7 @@ def test_workspace_linear_in_rows(lib):
 def test_plan_respects_budget(lib):
     for T, V, chunk in [(32768, 201088, 2048), (262144, 201088, 512), (4096, 32000, 1024), (1000, 1000, 1)]:
         q = B.backward_plan(B.make_problem(T, 2880, V, 100, chunk))
-        assert q["Tc"] * q["Vc"] <= max(chunk * V // 2, 128 * 128) or (q["Tc"] == 128)
+        tile = 256  # bf16 logit tile: 256 vocabulary x 256 token rows
+        assert q["Tc"] % tile == 0 and q["Vc"] % tile == 0
+        assert q["Tc"] * q["Vc"] <= max(chunk * V // 2, tile * tile) or q["Tc"] == tile
         assert q["nT"] * q["Tc"] >= T and q["nV"] * q["Vc"] >= V
