@@ -95,7 +95,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="synthetic workload id (0-4); 2 is the headline")
     ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -234,6 +236,15 @@ def main():
     }
     del H, W, idx, tl, mask, ws_f, ws_b, dH, dW
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        result["copy_calibration_bytes"] = 1 << 30
+        del src, dst
     if args.cpu_rows > 0:
         log(f"oracle CPU baseline on {args.cpu_rows} rows ...")
         result["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, x.T))

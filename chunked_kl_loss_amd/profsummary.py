@@ -1,0 +1,101 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m chunked_kl_loss_amd.profsummary trace <kernel_stats.csv> <out.md> "<command>"
+    python -m chunked_kl_loss_amd.profsummary traffic <fetch_counter.csv> <write_counter.csv> \\
+        <out.json> <workload> <steps>
+
+`trace` condenses a --kernel-trace --stats run into a markdown table grouped by
+kernel class.  `traffic` takes the FETCH_SIZE and WRITE_SIZE passes (KiB per
+dispatch), scales them by what the same counters read for the plain 1 GiB
+copy that bench.py --copy-calibration runs, and writes HBM bytes per launch
+for every kernel class, tagged with the hash of the kernel sources.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import json
+import sys
+
+CLASSES = (("fwd_lse", "fwd_lse"), ("bwd_grad", "bwd_grad"), ("gemm_store", "gemm_dhdw"),
+           ("transpose_pad", "transpose"), ("teacher_prep", "teacher_prep"),
+           ("fwd_finalize", "fwd_finalize"))
+
+
+def kernel_class(name: str) -> str:
+    for key, cls in CLASSES:
+        if key in name:
+            return cls
+    if "ckl" in name:
+        return "other"
+    if "copyBuffer" in name:  # the runtime's device-to-device copy (bench.py --copy-calibration)
+        return "copy"
+    return "foreign"
+
+
+def trace(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    agg = collections.OrderedDict()
+    for r in rows:
+        cls = kernel_class(r["Name"])
+        a = agg.setdefault(cls, [0, 0.0])
+        a[0] += int(r["Calls"])
+        a[1] += float(r["TotalDurationNs"])
+    tot = sum(v[1] for k, v in agg.items() if k != "foreign")
+    with open(out_md, "w") as f:
+        f.write(f"# rocprofv3 kernel trace: {command}\n\n")
+        f.write("| kernel class | launches | total ms | avg ms / launch | share |\n|---|---|---|---|---|\n")
+        for cls, (n, ns) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            if cls == "foreign":
+                continue
+            f.write(f"| {cls} | {n} | {ns / 1e6:.3f} | {ns / n / 1e6:.4f} | {100 * ns / tot:.1f}% |\n")
+        f.write("\nPer kernel symbol:\n\n| kernel | calls | avg ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                    f"{float(r['MaxNs']):.0f} |\n")
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    out = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            out.append((kernel_class(r["Kernel_Name"]), float(r["Counter_Value"]) * 1024.0))
+    return out
+
+
+def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, steps: int) -> None:
+    sys.path.insert(0, ".")
+    from bench import kernel_source_hash
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    copy_f = [b for c, b in fetch if c == "copy"]
+    copy_w = [b for c, b in write if c == "copy"]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy-calibration dispatch found (run bench.py --copy-calibration)")
+    gib = float(1 << 30)
+    fscale = gib / max(copy_f)  # counter bytes per true byte, from the 1 GiB copy
+    wscale = gib / max(copy_w)
+    res = {}
+    for name, data, scale in (("read", fetch, fscale), ("write", write, wscale)):
+        by = collections.defaultdict(list)
+        for c, b in data:
+            if c not in ("copy", "foreign"):
+                by[c].append(b * scale)
+        for c, v in by.items():
+            d = res.setdefault(c, {})
+            d[f"hbm_{name}_bytes_per_launch"] = sum(v) / len(v)
+            d["launches"] = len(v)
+    for c, d in res.items():
+        d["hbm_bytes_per_launch"] = d.get("hbm_read_bytes_per_launch", 0.0) + d.get("hbm_write_bytes_per_launch", 0.0)
+    json.dump({"workload": workload, "source_hash": kernel_source_hash(), "steps_profiled": steps,
+               "copy_scale": {"FETCH_SIZE": 1.0 / fscale, "WRITE_SIZE": 1.0 / wscale},
+               "kernels": res}, open(out_json, "w"), indent=1)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]))
+    else:
+        raise SystemExit(__doc__)

@@ -1,0 +1,180 @@
+"""GPU parity at full size (T up to 262,144 rows, V = 201,088, d = 2,880), in
+the launch configuration the benchmark times.
+
+At these sizes the fp64 oracle cannot evaluate everything, so the checks are:
+  * sampled rows computed one by one by the oracle (log-sum-exp, per-row KL,
+    rows of dH) -- stratified over first/last rows, G-block and tile
+    boundaries, document starts and random rows;
+  * for the 32K-row workload, sampled rows of dW from the oracle, which first
+    computes the fp64 log-sum-exp of every row (minutes of CPU);
+  * properties that hold at any size: the loss is the masked mean of the row
+    losses, masked rows give exact zeros, every column of dW sums to ~0
+    (each row of the logit gradient sums to 0), results are bitwise
+    reproducible;
+  * a closed form over the whole problem: with every vocabulary row of W
+    equal to c the student distribution is uniform, so LSE_t = h_t . c + ln V
+    and dW[v] = sum_t s_t (1/V - p_t[v]) h_t.
+Tolerances as in the element-wise tests (bf16 inputs: loss 2e-3 relative,
+dH / dW 1e-2 of the largest reference magnitude).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, make_inputs
+from tests.gpu_harness import TOL, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def inputs(cfg):
+    if cfg not in _cache:
+        _cache.clear()
+        say(f"generating workload {cfg} ...")
+        _cache[cfg] = make_inputs(cfg, seed=0)
+    return _cache[cfg]
+
+
+def sample_rows(x, chunk, n_random=24, seed=1):
+    import chunked_kl_loss_amd as ckl
+    plan = ckl.backward_plan(ckl.make_problem(x.T, x.d, x.V, x.K, chunk))
+    T = x.T
+    rows = {0, 1, 255, 256, T - 1, T - 2}
+    for b in range(1, plan["nT"]):
+        rows.update({b * plan["Tc"] - 1, b * plan["Tc"]})
+    if x.mask is not None:
+        starts = np.nonzero(np.diff(x.mask.astype(np.int8)) == 1)[0] + 1  # prompt span -> kept
+        rows.update(int(s) for s in starts[:8])
+        rows.update(int(s) - 1 for s in starts[:8])  # last masked row before each kept span
+    rng = np.random.default_rng(seed)
+    rows.update(int(r) for r in rng.integers(0, T, n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < T)), plan
+
+
+def check_rows(x, got, rows, grad_loss=1.0):
+    tol = TOL["bf16"]
+    ref = oracle.kl_rows(x.H, x.W, x.idx, x.tlogit, rows, mask=x.mask, grad_loss=grad_loss)
+    keep = np.ones(rows.size, bool) if x.mask is None else x.mask[rows] != 0
+    np.testing.assert_allclose(got["lse"][rows][keep], ref["lse"][keep], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(got["row_loss"][rows][keep], ref["row_loss"][keep], rtol=tol["loss_rel"],
+                               atol=tol["loss_rel"] * np.abs(ref["row_loss"][keep]).mean())
+    scale = np.abs(ref["dH"][keep]).max()
+    err = np.abs(got["dH"][rows][keep] - ref["dH"][keep]).max()
+    assert err <= tol["grad_rel"] * scale, (err, scale)
+    if (~keep).any():
+        assert (got["dH"][rows][~keep] == 0).all()
+        assert (got["lse"][rows][~keep] == 0).all() and (got["row_loss"][rows][~keep] == 0).all()
+    return err / scale
+
+
+def check_properties(x, got):
+    keep = np.ones(x.T, bool) if x.mask is None else x.mask != 0
+    N = int(keep.sum())
+    mean_rows = got["row_loss"][keep].sum() / N
+    assert abs(got["loss"] - mean_rows) <= 1e-5 * abs(mean_rows)
+    assert (got["dH"][~keep] == 0).all()
+    assert np.isfinite(got["dH"]).all() and np.isfinite(got["dW"]).all()
+    colsum = got["dW"].sum(axis=0)
+    colabs = np.abs(got["dW"]).sum(axis=0)
+    assert (np.abs(colsum) <= 2e-3 * colabs).all(), np.max(np.abs(colsum) / colabs)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_sampled_rows(cfg):
+    x = inputs(cfg)
+    rows, plan = sample_rows(x, x.chunk)
+    say(f"case cfg{cfg} full T={x.T} chunk={x.chunk} plan={plan} rows={rows.size}")
+    got = run_gpu(x)
+    e = check_rows(x, got, rows)
+    check_properties(x, got)
+    say(f"  sampled dH rel err {e:.2e}, loss {got['loss']:.6f}")
+
+
+def test_full_size_sampled_dw_rows_headline():
+    # dW rows need the log-sum-exp of every row: the oracle computes all of it
+    # in fp64 (the expensive part of this test).
+    x = inputs(2)
+    say(f"case cfg2 full dW rows T={x.T}")
+    got = run_gpu(x)
+    lse = oracle.lse_rows(x.H, x.W, block=512)
+    np.testing.assert_allclose(got["lse"], lse, rtol=0, atol=2e-3)
+    rng = np.random.default_rng(7)
+    vrows = np.unique(np.concatenate([[0, 1, x.V - 1, x.V - 2], rng.integers(0, x.V, 28),
+                                      x.idx[:4, 0].astype(np.int64)]))
+    ref = oracle.dw_rows(x.H, x.W, x.idx, x.tlogit, vrows, lse, mask=x.mask)
+    err = np.abs(got["dW"][vrows] - ref).max() / np.abs(ref).max()
+    say(f"  sampled dW rows rel err {err:.2e}")
+    assert err <= TOL["bf16"]["grad_rel"]
+
+
+def test_packed_documents_chunk_sweep():
+    x = inputs(4)
+    w = WORKLOADS[4]
+    base = None
+    for chunk in w.chunk_sweep:
+        rows, plan = sample_rows(x, chunk, n_random=16)
+        say(f"case cfg4 full T={x.T} chunk={chunk} plan={plan}")
+        got = run_gpu(x, chunk=chunk)
+        check_rows(x, got, rows)
+        check_properties(x, got)
+        if base is None:
+            base = got
+        else:
+            # the forward does not depend on chunk; the backward only reorders
+            # fp32 sums between G blocks (dW is fp32 out; dH is bf16 out, where
+            # a reordered sum may round one bf16 ulp = 2^-8 apart)
+            assert got["loss"] == base["loss"]
+            assert np.array_equal(got["lse"], base["lse"])
+            scale = np.abs(base["dW"]).max()
+            assert np.abs(got["dW"] - base["dW"]).max() <= 1e-3 * scale
+            assert np.abs(got["dH"] - base["dH"]).max() <= TOL["bf16"]["grad_rel"] * np.abs(base["dH"]).max()
+        del got
+
+
+def test_full_size_bitwise_reproducible():
+    x = inputs(2)
+    say("case cfg2 full determinism")
+    a = run_gpu(x)
+    b = run_gpu(x)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "row_loss", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_full_size_equal_rows_closed_form():
+    # every vocabulary row equal to c: q_t is uniform, so
+    #   LSE_t = h_t . c + ln V,  l_t = sum p log p + ln V,
+    #   dW[v] = sum_t s_t (1/V - P[t, v]) h_t,  dH = (sum_v G[t, v]) c ~ 0
+    import scipy.sparse as sp
+
+    from synth import Inputs, bf16_bits_to_f32
+    x0 = inputs(2)
+    rng = np.random.default_rng(3)
+    cbits = (rng.integers(0, 1 << 16, x0.d, dtype=np.uint32) & 0x3FFF | 0x3C00).astype(np.uint16)
+    cbits[rng.random(x0.d) < 0.5] |= 0x8000
+    Wb = np.tile(cbits, (x0.V, 1))
+    x = Inputs(T=x0.T, d=x0.d, V=x0.V, K=x0.K, chunk=x0.chunk, dtype="bf16", H=x0.H,
+               W=bf16_bits_to_f32(Wb), idx=x0.idx, tlogit=x0.tlogit, mask=None, H_bits=x0.H_bits, W_bits=Wb)
+    say("case cfg2 full closed form (equal vocabulary rows)")
+    got = run_gpu(x, grad_loss=0.5)
+    c = bf16_bits_to_f32(cbits).astype(np.float64)
+    hc = x.H.astype(np.float64) @ c
+    np.testing.assert_allclose(got["lse"], hc + math.log(x.V), rtol=0, atol=2e-3)
+    p = oracle.teacher_probs(x.tlogit)
+    ent = (p * np.log(p)).sum(axis=1)
+    np.testing.assert_allclose(got["row_loss"], ent + math.log(x.V), rtol=2e-3, atol=2e-3)
+    s = 0.5 / x.T
+    Pm = sp.csr_matrix((p.ravel(), x.idx.ravel().astype(np.int64),
+                        np.arange(0, x.T * x.K + 1, x.K)), shape=(x.T, x.V))
+    H64 = x.H.astype(np.float64)
+    dW_ref = s * (np.broadcast_to(H64.sum(axis=0) / x.V, (x.V, x.d)) - (Pm.T @ H64))
+    err = np.abs(got["dW"] - dW_ref).max() / np.abs(dW_ref).max()
+    say(f"  closed-form dW rel err {err:.2e}")
+    assert err <= TOL["bf16"]["grad_rel"]
+    # dH is (sum_v G[t, v]) c: zero up to the bf16 rounding of G
+    g_abs = s * 2.0  # sum_v |G[t, v]| <= s (M + sum p) = 2 s
+    assert np.abs(got["dH"]).max() <= 1e-2 * g_abs * np.abs(c).max()
