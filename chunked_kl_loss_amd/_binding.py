@@ -112,9 +112,9 @@ def workspace_size(prob: Problem, which: int) -> int:
 
 def backward_plan(prob: Problem):
     lib = load_library()
-    out = (ctypes.c_int64 * 4)()
+    out = (ctypes.c_int64 * 5)()
     check(lib.ckl_backward_plan(ctypes.byref(prob), out), lib)
-    return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3])
+    return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3], n_buffers=out[4])
 
 
 KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dhdw", "reserved5", "transpose",

@@ -41,6 +41,16 @@ ckl_status hip_fail(hipError_t e, const char* what) {
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 constexpr int kTargetWorkgroups = 2048;  // fused kernels: row blocks x vocabulary splits
+// The backward keeps one G block, stored as G and G^T, within chunk * V
+// elements.  (Double-buffering it to overlap the recompute of block i+1 with
+// the contraction of block i on a second stream measured no faster: both
+// kernels are throughput-bound, so concurrency only splits the CUs.)
+constexpr int kGBuffers = 1;
+// Row padding (elements) of every matrix whose leading dimension the library
+// picks (H^T, W^T, G, G^T): 256 bytes keeps the stride away from large powers
+// of two, so the 16 rows one global->LDS load touches spread over memory
+// channels instead of all hitting one.
+constexpr int64_t kLdPad = 128;
 
 // ------------------------------------------------------------------ timing --
 struct TimingState {
@@ -149,7 +159,7 @@ Plan make_plan(const ckl_problem* p) {
   // G^T), within chunk * V elements in total.  Among the admissible shapes pick
   // the one with the least fp32 read-modify-write of dH (once per extra
   // vocabulary block) and dW (once per extra token block).
-  const int64_t per_layout = std::max<int64_t>(p->chunk * p->V / 2, q.BM * q.BN);
+  const int64_t per_layout = std::max<int64_t>(p->chunk * p->V / (2 * kGBuffers), q.BM * q.BN);
   double best = -1.0;
   for (int64_t nT = 1; nT <= q.Tp / q.BN; ++nT) {
     const int64_t Tc = round_up(ceil_div(q.Tp, nT), q.BN);
@@ -191,7 +201,7 @@ FwdWs fwd_layout(const Plan& q) {
 }
 
 struct BwdWs {
-  size_t idx_s, p_s, M, s, N, bad, Ht, Wt, G, Gt, dH, dW, total;
+  size_t idx_s, p_s, M, s, N, bad, Ht, Wt, G[kGBuffers], Gt[kGBuffers], dH, dW, total;
 };
 BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   BwdWs w{};
@@ -203,10 +213,12 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   w.s = take(q.Tp * 4);
   w.N = take(4);
   w.bad = take(4);
-  w.Ht = take((size_t)q.d * q.Tp * q.esz);
-  w.Wt = take((size_t)q.d * q.Vp * q.esz);
-  w.G = take((size_t)q.Tc * q.Vc * q.esz);
-  w.Gt = take((size_t)q.Tc * q.Vc * q.esz);
+  w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
+  w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
+  for (int i = 0; i < kGBuffers; ++i) {
+    w.G[i] = take((size_t)q.Tc * (q.Vc + kLdPad) * q.esz);
+    w.Gt[i] = take((size_t)q.Vc * (q.Tc + kLdPad) * q.esz);
+  }
   w.dH = p->dh_dtype == CKL_BF16 ? take((size_t)q.T * q.d * 4) : 0;
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
   w.total = o;
@@ -314,8 +326,12 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   int* bad = (int*)(b + w.bad);
   void* Ht = b + w.Ht;
   void* Wt = b + w.Wt;
-  void* G = b + w.G;
-  void* Gt = b + w.Gt;
+  void* Gbuf[kGBuffers];
+  void* Gtbuf[kGBuffers];
+  for (int i = 0; i < kGBuffers; ++i) {
+    Gbuf[i] = b + w.G[i];
+    Gtbuf[i] = b + w.Gt[i];
+  }
   float* dHacc = p->dh_dtype == CKL_BF16 ? (float*)(b + w.dH) : (float*)dH;
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
@@ -335,10 +351,10 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st); }),
           "row_scale");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp, st); }),
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp + kLdPad, st); }),
           "transpose H");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp, st); }),
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp + kLdPad, st); }),
           "transpose W");
 
   const char* Htb = (const char*)Ht;
@@ -349,20 +365,22 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
     for (int64_t tb = 0; tb < q.nT; ++tb) {
       const int64_t tb0 = tb * q.Tc;
       const int64_t trows = std::min(q.Tc, q.Tp - tb0);
+      void* G = Gbuf[0];
+      void* Gt = Gtbuf[0];
       int64_t splits, tps;
       pick_splits(trows / q.BN, vrows / q.BM, &splits, &tps);
       HIP_TRY(timed(CKL_KERNEL_BWD_GRAD, st,
                     [&] {
                       return ckl::launch_bwd_grad(q.in_bf16, H, W, T, d, V, K, idx_s, p_s, M, lse, srow, (int)tb0,
-                                                  (int)trows, (int)vb0, (int)vrows, (int)splits, (int)tps, G, vrows,
-                                                  Gt, trows, st);
+                                                  (int)trows, (int)vb0, (int)vrows, (int)splits, (int)tps, G,
+                                                  vrows + kLdPad, Gt, trows + kLdPad, st);
                     }),
               "bwd_grad");
       // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)  (longer k: scheduled first)
       // dH[tb0 .. tb0 + trows) (+)= G W[vb0 .. vb0 + vrows)
-      const ckl::GemmArgs gdw{Gt, trows, Htb + tb0 * q.esz, q.Tp, dWacc + vb0 * q.d, q.d,
+      const ckl::GemmArgs gdw{Gt, trows + kLdPad, Htb + tb0 * q.esz, q.Tp + kLdPad, dWacc + vb0 * q.d, q.d,
                               (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
-      const ckl::GemmArgs gdh{G, vrows, Wtb + vb0 * q.esz, q.Vp, dHacc + tb0 * q.d, q.d,
+      const ckl::GemmArgs gdh{G, vrows + kLdPad, Wtb + vb0 * q.esz, q.Vp + kLdPad, dHacc + tb0 * q.d, q.d,
                               (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
       HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdw, gdh, st); }),
               "gemm dW + dH");
@@ -377,7 +395,7 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   return CKL_OK;
 }
 
-ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]) {
+ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
   if (!out) return fail(CKL_ERR_INVALID_ARG, "out is NULL");
@@ -386,6 +404,7 @@ ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]) {
   out[1] = q.Vc;
   out[2] = q.nT;
   out[3] = q.nV;
+  out[4] = kGBuffers;
   return CKL_OK;
 }
 

@@ -13,6 +13,8 @@
 // next slice is fetched into registers while the current one is multiplied.
 #pragma once
 
+#include <type_traits>
+
 #include "ckl_common.hpp"
 
 namespace ckl {
@@ -629,38 +631,46 @@ __device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __re
     }
     mma(cur);
   };
-  // the same step when every slice involved is whole and in range: one basic
-  // block, with MFMAs interleaved one-for-one with the LDS reads and DMA
-  // issues so that the matrix core never waits for the issue of either
+  // The same step when every slice involved is whole and in range, in one
+  // fixed order: MFMA j of the current slice is followed by the j-th DMA of
+  // the refill (issued first, to give it the most time) and then by the LDS
+  // fragment reads of the next slice, one per MFMA.  Scheduling barriers pin
+  // the order (the scheduler would otherwise bunch the DMAs, stalling the
+  // only wave of the SIMD on the address queue).
+  const int fx = wave_m * C::WM, fy = wave_n * C::WN;
   auto step_full = [&](int kt, const Frags<C>& cur, Frags<C>& nxt) {
-    __builtin_amdgcn_sched_barrier(0);  // keep the waits below out of the previous step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     wait_lgkm0();
     wait_vmcnt<(C::NSTAGE - 3) * C::LOADS_PER_STAGE>();
     phase_barrier();
-    {
-      char* st = smem + ((kt + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE_BYTES;
-      const int k0 = (kt + C::NSTAGE - 1) * C::BK;
+    char* dst = smem + ((kt + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE_BYTES;
+    const int k0 = (kt + C::NSTAGE - 1) * C::BK;
+    const char* src = smem + ((kt + 1) % C::NSTAGE) * C::STAGE_BYTES;
+    constexpr int kMfma = 2 * C::MB * C::NB;
+    constexpr int kReads = 2 * (C::MB + C::NB);
+    static_assert(C::LOADS_PER_STAGE + kReads <= kMfma, "one memory op per MFMA");
 #pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) lds_dma16(X + k0 + xoff[i], st + (wave + i * C::NWAVES) * 1024);
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i)
-        lds_dma16(Y + k0 + yoff[i], st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
+    for (int j = 0; j < kMfma; ++j) {
+      {
+        const int s = j / (C::MB * C::NB), mb = (j / C::NB) % C::MB, nb = j % C::NB;
+        tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[s][mb], cur.b[s][nb], tile.acc[mb][nb], 0, 0, 0);
+      }
+      if (j < C::X_LOADS) {
+        lds_dma16(X + k0 + xoff[j], dst + (wave + j * C::NWAVES) * 1024);
+      } else if (j < C::LOADS_PER_STAGE) {
+        const int i = j - C::X_LOADS;
+        lds_dma16(Y + k0 + yoff[i], dst + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
+      } else if (j < C::LOADS_PER_STAGE + kReads) {
+        const int q = j - C::LOADS_PER_STAGE;
+        const int s = q / (C::MB + C::NB), w = q % (C::MB + C::NB);
+        if (w < C::MB)
+          nxt.a[s][w] = *reinterpret_cast<const bf16x8*>(src + (fx + w * 32) * C::ROW_BYTES + roff[s]);
+        else
+          nxt.b[s][w - C::MB] =
+              *reinterpret_cast<const bf16x8*>(src + C::X_BYTES + (fy + (w - C::MB) * 32) * C::ROW_BYTES + roff[s]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    read(kt + 1, nxt);
-    mma(cur);
-    constexpr int kReads = 2 * (C::MB + C::NB), kMfma = 2 * C::MB * C::NB, kDma = C::LOADS_PER_STAGE;
-    static_assert(kReads + kDma <= kMfma, "interleave pattern");
-#pragma unroll
-    for (int i = 0; i < kReads; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-#pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global->LDS load
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads - kDma, 0);
   };
 
 #pragma unroll
@@ -682,6 +692,239 @@ __device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __re
     step(kt + 1, fb, fa);
   }
   if (kt < nk) step(kt, fa, fb);
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 main loop on 64-wide k slices in two LDS stages.
+//
+// A stage row holds 64 k values = 128 bytes = eight 16-byte chunks, so one
+// global_load_lds instruction of a wave moves 8 rows x 128 bytes, i.e. whole
+// cache lines: half the texture-address and L1 requests per byte of the
+// 32-wide layout, whose instructions touch sixteen half lines.  Chunk c of
+// row r sits in slot c ^ ((r >> 1) & 7): with 64 four-byte banks the sixteen
+// lanes of a ds_read_b128 quarter-wave (sixteen consecutive rows, one chunk)
+// then fall in sixteen distinct 16-byte bank groups.
+//
+// Two stages fill 128 KiB, so the pipeline runs on half stages: half-step h
+// multiplies k16 substeps 2 (h & 1) and 2 (h & 1) + 1 of stage h >> 1 from
+// registers while the LDS fragments of half-step h + 1 are read.  At the
+// start of each odd half-step every wave has read all of its stage (LDS
+// counter drained, then a barrier), and this thread's loads of the next
+// stage are complete (vmcnt 0): after the barrier the stage just finished is
+// refilled with slice s + 2, its loads spread over that half-step's MFMAs.
+// ---------------------------------------------------------------------------
+//
+// PIPE = 0 drops the register double-buffering of the fragments (for kernels
+// whose epilogue state leaves no room for it): each stage is then read and
+// multiplied one k16 substep at a time, and the finished stage is refilled
+// right after the barrier that starts the next one.
+template <int BM_, int BN_, int WM_, int WN_, int PIPE_ = 1>
+struct Dma64Cfg {
+  using TIn = bf16_t;
+  using TileT = DmaTile<Dma64Cfg>;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 2, PIPE = PIPE_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NTHREADS = 64 * NWAVES;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static constexpr int BK = 64;
+  static constexpr int ROW_BYTES = 128;
+  static constexpr int X_BYTES = BM * ROW_BYTES, Y_BYTES = BN * ROW_BYTES;
+  static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  // one wave-instruction fills 8 rows; loads per thread per stage
+  static constexpr int X_LOADS = BM / 8 / NWAVES, Y_LOADS = BN / 8 / NWAVES;
+  static constexpr int LOADS_PER_STAGE = X_LOADS + Y_LOADS;
+  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "row groups per wave");
+  static_assert(NWAVES % 2 == 0, "the row groups of a wave share one swizzle phase");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// Same contract as tile_mma_dma (kdim a multiple of 8; k past kdim reads as
+// zero; rows past xrows / yrows give garbage outputs to discard; 32-bit row
+// offsets; ends with a barrier).
+template <class C>
+__device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
+                                             const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
+                                             char* smem) {
+  static_assert(C::BK == 64 && C::NSTAGE == 2, "two 64-wide stages");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave / C::WAVES_N;
+  const int wave_n = wave % C::WAVES_N;
+
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
+
+  // Loader: lane -> (row within its 8-row group, slot).  The rows of load i
+  // are (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for every
+  // i since NWAVES is even.
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
+  uint32_t off[C::LOADS_PER_STAGE];
+#pragma unroll
+  for (int i = 0; i < C::X_LOADS; ++i) {
+    const int row = (wave + i * C::NWAVES) * 8 + lrow;
+    off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < C::Y_LOADS; ++i) {
+    const int row = (wave + i * C::NWAVES) * 8 + lrow;
+    off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
+  }
+  auto lds_at = [&](int kt, int i) {
+    char* st = smem + (kt & 1) * C::STAGE_BYTES;
+    return i < C::X_LOADS ? st + (wave + i * C::NWAVES) * 1024
+                          : st + C::X_BYTES + (wave + (i - C::X_LOADS) * C::NWAVES) * 1024;
+  };
+  // load i of slice kt; `whole`: the slice lies inside [0, kdim)
+  auto dma = [&](int kt, int i, bool whole) {
+    const int k0 = kt * C::BK;
+    const bf16_t* src = (i < C::X_LOADS ? X : Y) + k0 + off[i];
+    const void* g = (whole || k0 + lchunk * 8 < kdim) ? (const void*)src : (const void*)kZeroChunk;
+    lds_dma16(g, lds_at(kt, i));
+  };
+
+  // Reader: lane reads row (lane & 31) + 32 block of its wave's rows, chunk
+  // 2 sub + (lane >> 5) for k16 substep sub of the stage.
+  const int rrow = lane & 31;
+  const int rsw = (rrow >> 1) & 7;
+  int roff[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) roff[sub] = rrow * C::ROW_BYTES + (((2 * sub + (lane >> 5)) ^ rsw) * 16);
+  const int xwave = wave_m * C::WM * C::ROW_BYTES;
+  const int ywave = C::X_BYTES + wave_n * C::WN * C::ROW_BYTES;
+  // fragment q (substep q / (MB + NB); X blocks, then Y blocks) of the half
+  // stage `odd` of stage kt
+  auto read = [&](int kt, auto odd, Frags<C>& f, int q) {
+    const char* st = smem + (kt & 1) * C::STAGE_BYTES;
+    const int s = q / (C::MB + C::NB), w = q % (C::MB + C::NB);
+    const int sub = 2 * decltype(odd)::value + s;
+    if (w < C::MB)
+      f.a[s][w] = *reinterpret_cast<const bf16x8*>(st + xwave + w * 32 * C::ROW_BYTES + roff[sub]);
+    else
+      f.b[s][w - C::MB] = *reinterpret_cast<const bf16x8*>(st + ywave + (w - C::MB) * 32 * C::ROW_BYTES + roff[sub]);
+  };
+  constexpr int kMfma = 2 * C::MB * C::NB;
+  constexpr int kReads = 2 * (C::MB + C::NB);
+  constexpr int kDma = C::LOADS_PER_STAGE;
+  auto mfma = [&](const Frags<C>& f, int j) {
+    const int s = j / (C::MB * C::NB), mb = (j / C::NB) % C::MB, nb = j % C::NB;
+    tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][mb], f.b[s][nb], tile.acc[mb][nb], 0, 0, 0);
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  // half-step 2 kt: the next fragments come from the same stage; the reads
+  // are spread evenly over the MFMAs
+  auto half_even = [&](int kt, const Frags<C>& cur, Frags<C>& nxt) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+#pragma unroll
+    for (int j = 0; j < kMfma; ++j) {
+      mfma(cur, j);
+#pragma unroll
+      for (int q = j * kReads / kMfma; q < (j + 1) * kReads / kMfma; ++q) read(kt, Odd{}, nxt, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // half-step 2 kt + 1: refill stage kt with slice kt + 2 (its loads first,
+  // to give them the most time), then read the first half of stage kt + 1
+  auto half_odd = [&](int kt, const Frags<C>& cur, Frags<C>& nxt, bool next, bool refill, bool whole) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+    if (next) {
+      wait_vmcnt<0>();
+      phase_barrier();
+    }
+#pragma unroll
+    for (int j = 0; j < kMfma; ++j) {
+      mfma(cur, j);
+#pragma unroll
+      for (int q = j * (kDma + kReads) / kMfma; q < (j + 1) * (kDma + kReads) / kMfma; ++q) {
+        if (q < kDma) {
+          if (refill) dma(kt + 2, q, whole);
+        } else if (next) {
+          read(kt + 1, Even{}, nxt, q - kDma);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nk = (kdim + C::BK - 1) / C::BK;
+  const int n_full = kdim / C::BK;
+  if constexpr (!C::PIPE) {
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
+      if (nk > 1) {
+#pragma unroll
+        for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
+        wait_vmcnt<kDma>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt > 0) {
+        // only stage kt is in flight; the barrier also ends every wave's
+        // reads of stage kt - 1, whose buffer takes slice kt + 1
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < nk) {
+          const bool whole = kt + 1 < n_full;
+#pragma unroll
+          for (int i = 0; i < kDma; ++i) dma(kt + 1, i, whole);
+        }
+      }
+      const char* st = smem + (kt & 1) * C::STAGE_BYTES;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        bf16x8 a[C::MB], b[C::NB];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+          a[mb] = *reinterpret_cast<const bf16x8*>(st + xwave + mb * 32 * C::ROW_BYTES + roff[sub]);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+          b[nb] = *reinterpret_cast<const bf16x8*>(st + ywave + nb * 32 * C::ROW_BYTES + roff[sub]);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], tile.acc[mb][nb], 0, 0, 0);
+      }
+    }
+  } else if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
+      wait_vmcnt<kDma>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    phase_barrier();
+    Frags<C> fa, fb;
+#pragma unroll
+    for (int q = 0; q < kReads; ++q) read(0, Even{}, fa, q);
+    int kt = 0;
+    for (; kt + 2 < n_full; ++kt) {  // steady state: the refilled slice is whole
+      half_even(kt, fa, fb);
+      half_odd(kt, fb, fa, true, true, true);
+    }
+    for (; kt < nk; ++kt) {
+      half_even(kt, fa, fb);
+      half_odd(kt, fb, fa, kt + 1 < nk, kt + 2 < nk, kt + 2 < n_full);
+    }
+  }
   __syncthreads();
 }
 
@@ -720,7 +963,8 @@ __device__ __forceinline__ void run_mma(Tile<C>& t, const typename C::TIn* X, in
 template <class C>
 __device__ __forceinline__ void run_mma(DmaTile<C>& t, const bf16_t* X, int64_t ldx, int xrows, const bf16_t* Y,
                                         int64_t ldy, int yrows, int kdim, char* smem) {
-  if constexpr (C::NWAVES == 4) tile_mma_sp<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
+  if constexpr (C::BK == 64) tile_mma_k64<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
+  else if constexpr (C::NWAVES == 4) tile_mma_sp<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
   else tile_mma_dma<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
 }
 

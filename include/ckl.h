@@ -124,10 +124,12 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
 
 /* The G-block plan ckl_backward uses for problem *p: out[0] = Tc (token rows
  * per block), out[1] = Vc (vocabulary columns per block), out[2] = number of
- * token blocks, out[3] = number of vocabulary blocks.  dW is read-modified-
+ * token blocks, out[3] = number of vocabulary blocks, out[4] = number of G
+ * blocks held at once (each stored as G [Tc, Vc] and its transpose; all of
+ * them together within about chunk * V elements).  dW is read-modified-
  * written once per extra token block and dH once per extra vocabulary block.
  * Host-only; touches no device. */
-ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[4]);
+ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
 
 /* Kernel classes for the timing records below. */
 typedef enum {

@@ -109,8 +109,8 @@ def test_workspace_linear_in_rows(lib):
     def ws(T):
         prob = B.make_problem(T, 2880, 201088, 100, 2048)
         q = B.backward_plan(prob)
-        g_block = 2 * q["Tc"] * q["Vc"] * 2          # G and G^T, bf16
-        assert g_block <= 2048 * 201088 * 2 * 1.01  # bounded by the chunk budget
+        g_block = q["n_buffers"] * 2 * q["Tc"] * q["Vc"] * 2  # G and G^T per buffer, bf16
+        assert g_block <= 2048 * 201088 * 2 * 1.01             # bounded by the chunk budget
         return B.workspace_size(prob, 1) - g_block
     a, b, c = ws(32768), ws(65536), ws(131072)
     assert c - b == pytest.approx(2 * (b - a), rel=1e-4)
@@ -123,5 +123,5 @@ def test_plan_respects_budget(lib):
         q = B.backward_plan(B.make_problem(T, 2880, V, 100, chunk))
         tile = 256  # bf16 logit tile: 256 vocabulary x 256 token rows
         assert q["Tc"] % tile == 0 and q["Vc"] % tile == 0
-        assert q["Tc"] * q["Vc"] <= max(chunk * V // 2, tile * tile) or q["Tc"] == tile
+        assert q["n_buffers"] * q["Tc"] * q["Vc"] <= max(chunk * V // 2, tile * tile) or q["Tc"] == tile
         assert q["nT"] * q["Tc"] >= T and q["nV"] * q["Vc"] >= V
