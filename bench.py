@@ -2,17 +2,21 @@
 """Benchmark of the fused chunked forward-KL loss (forward + backward) on one
 MI355X.
 
-One step = ckl_forward + ckl_backward over one batch of synthetic inputs that
-are resident in HBM before timing starts.  Default workload: T = 32,768 rows,
-d = 2,880, V = 201,088, K = 100 cached teacher entries, chunk = 2,048, bf16 H
-and W (the pages' 32K-context, 201,088-token-vocabulary case).
+One step = the loss and its gradients dH, dW over one batch of synthetic
+inputs that are resident in HBM before timing starts, either as
+ckl_forward + ckl_backward (--path recompute: the backward recomputes the
+logits chunk by chunk) or as one ckl_forward_backward call (--path fused: each
+row chunk's logits are multiplied once and kept).  Default workload:
+T = 32,768 rows, d = 2,880, V = 201,088, K = 100 cached teacher entries,
+chunk = 2,048, bf16 H and W (the pages' 32K-context, 201,088-token-vocabulary
+case).
 
 Prints ONE JSON line with tokens/s, TFLOP/s (8 T V d useful flops per step),
 the fraction of the bf16 dense MFMA peak, peak HBM, a roofline entry for the
 dominant kernel (timed live with HIP events on the launch stream) and the fp64
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload 2]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload 2] [--path fused|recompute]
 """
 from __future__ import annotations
 
@@ -96,6 +100,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--path", choices=("fused", "recompute"), default="fused",
+                    help="one ckl_forward_backward call per step, or ckl_forward + ckl_backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -131,9 +137,10 @@ def main():
     T, d, V, K = x.T, x.d, x.V, x.K
     in_code = B.CKL_BF16 if x.dtype == "bf16" else B.CKL_F32
     prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32)
-    plan = B.backward_plan(prob)
-    ws_f = torch.empty(B.workspace_size(prob, 0), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
+    fused = args.path == "fused"
+    plan = B.fused_plan(prob) if fused else B.backward_plan(prob)
+    ws_f = torch.empty(B.workspace_size(prob, 2 if fused else 0), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(1 if fused else B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
     dH = torch.empty((T, d), dtype=H.dtype, device=dev)
@@ -151,7 +158,14 @@ def main():
         B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, lse.data_ptr(),
                                  None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(), ws_b.numel(), sp), lib)
 
-    log(f"warmup {args.warmup} steps; backward plan {plan}")
+    def both():
+        B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, None,
+                                         loss.data_ptr(), lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(),
+                                         ws_f.data_ptr(), ws_f.numel(), sp), lib)
+
+    if fused:
+        fwd, bwd = both, (lambda: None)
+    log(f"warmup {args.warmup} steps; path {args.path}, plan {plan}")
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -182,7 +196,9 @@ def main():
     # ---- per-kernel timing and roofline of the dominant kernel
     kt = ckl.timing_read()
     flops_step = 8.0 * T * V * d
-    algo_flops = {"fwd_lse": 2.0 * T * V * d, "bwd_grad": 2.0 * T * V * d, "gemm_dhdw": 4.0 * T * V * d}
+    algo_flops = {"fwd_lse": 2.0 * T * V * d, "gemm_dhdw": 4.0 * T * V * d}
+    if not fused:
+        algo_flops["bwd_grad"] = 2.0 * T * V * d
     kernels = {k: {"total_ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
                    "avg_launch_ms": (ms / n if n else 0.0)} for k, (ms, n) in kt.items()}
     dom = max(algo_flops, key=lambda k: kt[k][0])
@@ -221,15 +237,16 @@ def main():
         "data": "synthetic (seeded generator: H~N(0,1), W~N(0,1/d), K distinct uniform teacher indices, "
                 "teacher logits N(0,2) sorted)",
         "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "chunk": chunk,
-                   "masked_rows": T - n_valid, "parallelism": "single GPU",
-                   "backward_plan": plan},
+                   "masked_rows": T - n_valid, "parallelism": "single GPU", "path": args.path,
+                   "plan": plan},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "tflops_note": "8 T V d useful flops per step (forward, recomputed logits, dH, dW); the fused path "
+                       "multiplies 6 T V d of them" if fused else "8 T V d flops per step, all multiplied",
         "peak_hbm_gib": peak_gib,
-        "fwd_ms": float(np.mean(fwd_ms)),
-        "bwd_ms": float(np.mean(bwd_ms)),
-        "fwd_ms_min": float(np.min(fwd_ms)),
-        "bwd_ms_min": float(np.min(bwd_ms)),
+        "fwd_ms": None if fused else float(np.mean(fwd_ms)),
+        "bwd_ms": None if fused else float(np.mean(bwd_ms)),
+        "step_ms_events_min": float(np.min(np.add(fwd_ms, bwd_ms))),
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,

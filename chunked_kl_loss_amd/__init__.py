@@ -6,7 +6,11 @@ computed by hand-written HIP kernels behind the C ABI in include/ckl.h:
     loss, lse, _ = forward(H, W, idx, tlogit, mask, chunk)
     dH, dW = backward(H, W, idx, tlogit, mask, lse, grad_loss, chunk)
 
-or, through autograd, ``chunked_kl_loss(H, W, idx, tlogit, mask, chunk)``.
+or, in one call without recomputing the logits,
+
+    loss, lse, _, dH, dW = forward_backward(H, W, idx, tlogit, mask, grad_loss, chunk)
+
+or, through autograd, ``chunked_kl_loss(H, W, idx, tlogit, mask, chunk, fused=False)``.
 """
 from ._binding import (  # noqa: F401
     CKL_BF16,
@@ -16,10 +20,12 @@ from ._binding import (  # noqa: F401
     backward,
     backward_plan,
     forward,
+    forward_backward,
+    fused_plan,
     load_library,
     make_problem,
     timing_enable,
     timing_read,
     workspace_size,
 )
-from .autograd import ChunkedKLLoss, chunked_kl_loss  # noqa: F401
+from .autograd import ChunkedKLLoss, FusedChunkedKLLoss, chunked_kl_loss  # noqa: F401

@@ -26,6 +26,8 @@ EXPORTED = (
     "ckl_forward",
     "ckl_backward",
     "ckl_backward_plan",
+    "ckl_forward_backward",
+    "ckl_fused_plan",
     "ckl_timing_enable",
     "ckl_timing_read",
     "ckl_status_string",
@@ -77,6 +79,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckl_backward.restype = i32
     lib.ckl_backward_plan.argtypes = [P, i64p]
     lib.ckl_backward_plan.restype = i32
+    lib.ckl_forward_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ckl_forward_backward.restype = i32
+    lib.ckl_fused_plan.argtypes = [P, i64p]
+    lib.ckl_fused_plan.restype = i32
     lib.ckl_timing_enable.argtypes = [ctypes.c_int]
     lib.ckl_timing_enable.restype = i32
     lib.ckl_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), i64p]
@@ -117,7 +123,15 @@ def backward_plan(prob: Problem):
     return dict(Tc=out[0], Vc=out[1], nT=out[2], nV=out[3], n_buffers=out[4])
 
 
-KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dhdw", "reserved5", "transpose",
+def fused_plan(prob: Problem):
+    """Row chunks and dH split-k of ckl_forward_backward for this problem."""
+    lib = load_library()
+    out = (ctypes.c_int64 * 4)()
+    check(lib.ckl_fused_plan(ctypes.byref(prob), out), lib)
+    return dict(rows=out[0], chunks=out[1], dh_parts=out[2], part_cols=out[3])
+
+
+KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dhdw", "g_pass", "transpose",
                   "other")
 
 
@@ -229,3 +243,33 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     check(lib.ckl_backward(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlogit), _ptr(m), _ptr(lse),
                            _ptr(grad_loss), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
     return dH, dW
+
+
+def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 2048, dh_dtype=None,
+                     dw_dtype=None, validate: bool = False, want_row_loss: bool = False):
+    """One call, no logit recompute: returns (loss [1], lse [T], row_loss [T] or None, dH, dW), the
+    gradients being those of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
+    torch = _torch()
+    _check_inputs(H, W, idx, tlogit, mask)
+    T, d = H.shape
+    V, K = W.shape[0], idx.shape[1]
+    in_code = _dtype_code(H.dtype)
+    dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
+    dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate)
+    lib = load_library()
+    ws_bytes = workspace_size(prob, 2)
+    dev = H.device
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    dH = torch.empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
+    dW = torch.empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
+    m = mask.view(torch.uint8) if mask is not None else None
+    if grad_loss is not None:
+        grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    check(lib.ckl_forward_backward(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlogit), _ptr(m),
+                                   _ptr(grad_loss), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(dH), _ptr(dW),
+                                   _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
+    return loss, lse, row_loss, dH, dW

@@ -1,5 +1,11 @@
-"""torch.autograd wrapper: the forward saves (H, W, idx, tlogit, mask, lse) and
-the backward recomputes the logit tiles inside libckl."""
+"""torch.autograd wrappers.
+
+ChunkedKLLoss: the forward saves (H, W, idx, tlogit, mask, lse) and the
+backward recomputes the logit tiles inside libckl.
+
+FusedChunkedKLLoss: one library call in the forward computes the loss and the
+gradients of the loss itself (no recompute); the backward only scales them by
+the incoming gradient (1 for a loss that is backpropagated directly)."""
 from __future__ import annotations
 
 import torch
@@ -26,7 +32,25 @@ class ChunkedKLLoss(torch.autograd.Function):
         return dH, dW, None, None, None, None
 
 
-def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048):
+class FusedChunkedKLLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048):
+        loss, _, _, dH, dW = _binding.forward_backward(H, W, idx, tlogit, mask, None, chunk=chunk,
+                                                       dh_dtype=H.dtype, dw_dtype=W.dtype)
+        ctx.save_for_backward(dH, dW)
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, grad):
+        dH, dW = ctx.saved_tensors
+        g = grad.to(torch.float32)
+        return ((dH.float() * g).to(dH.dtype), (dW.float() * g).to(dW.dtype), None, None, None, None)
+
+
+def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False):
     """Mean forward KL(teacher || student) over unmasked rows, differentiable
-    with respect to H and W."""
+    with respect to H and W.  fused=True computes the gradients together with
+    the loss (one pass over the logits, chunk x V extra workspace)."""
+    if fused:
+        return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk)
     return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk)

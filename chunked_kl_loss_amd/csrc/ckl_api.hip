@@ -40,7 +40,11 @@ ckl_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
-constexpr int kTargetWorkgroups = 2048;  // fused kernels: row blocks x vocabulary splits
+// Compute units of an MI355X; the logit and contraction kernels fit one
+// workgroup per CU (128 KiB of LDS each), so kCUs workgroups make one wave.
+constexpr int64_t kCUs = 256;
+// dH split-k parts of the fused call: about this many dH tiles per chunk.
+constexpr int64_t kSplitTiles = 1024;
 // The backward keeps one G block, stored as G and G^T, within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
 // the contraction of block i on a second stream measured no faster: both
@@ -116,15 +120,29 @@ struct Plan {
   int64_t f_splits, f_tps;
   // backward G blocks
   int64_t Tc, Vc, nT, nV;
+  // fused forward + backward: row chunks of Cs rows, nS of them; forward
+  // splits per chunk; dH split-k into Sh parts of Vs vocabulary columns
+  int64_t Cs, nS, c_splits, c_tps, Sh, Vs, groups;
 };
 
-// Vocabulary splits of the fused kernels: enough workgroups to fill the chip
-// several times while every split keeps a run of tiles (the teacher cursors
-// advance monotonically along a split).
+// Vocabulary splits of the logit kernels: each workgroup sweeps a run of
+// tiles_per_split vocabulary tiles for one block of rows (the teacher cursors
+// advance monotonically along a split).  Picks the split count with the
+// shortest makespan in tile-times, ceil(workgroups / kCUs) x tiles_per_split,
+// and among equals the fewest splits.
 void pick_splits(int64_t row_blocks, int64_t vtiles, int64_t* splits, int64_t* tps) {
-  int64_t s = std::max<int64_t>(1, std::min<int64_t>(vtiles, ceil_div(kTargetWorkgroups, row_blocks)));
-  *tps = ceil_div(vtiles, s);
-  *splits = ceil_div(vtiles, *tps);
+  int64_t best = -1;
+  for (int64_t s = 1; s <= vtiles; ++s) {
+    const int64_t t = ceil_div(vtiles, s);
+    const int64_t sp = ceil_div(vtiles, t);
+    if (sp != s) continue;  // the same split as a smaller count
+    const int64_t cost = ceil_div(row_blocks * sp, kCUs) * t;
+    if (best < 0 || cost < best) {
+      best = cost;
+      *splits = sp;
+      *tps = t;
+    }
+  }
 }
 
 ckl_status check_problem(const ckl_problem* p) {
@@ -177,6 +195,18 @@ Plan make_plan(const ckl_problem* p) {
       q.Tc = Tc; q.Vc = Vc; q.nT = nTr; q.nV = ceil_div(q.Vp, Vc);
     }
   }
+
+  // Fused call: chunks of `chunk` rows in whole 256-row blocks (the loss
+  // block sums are per 256 rows), at most the padded row count.
+  q.Cs = std::min(round_up(p->chunk, 256), round_up(q.Tp, 256));
+  q.nS = ceil_div(q.Tp, q.Cs);
+  pick_splits(q.Cs / q.BN, q.Vp / q.BM, &q.c_splits, &q.c_tps);
+  const int64_t gtile = ckl::gemm_tile(q.in_bf16);
+  const int64_t dh_tiles = ceil_div(q.Cs, gtile) * ceil_div(q.d, gtile);
+  const int64_t sh = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kSplitTiles, dh_tiles), q.Vp / 256));
+  q.Vs = round_up(ceil_div(q.Vp, sh), 256);
+  q.Sh = ceil_div(q.Vp, q.Vs);
+  q.groups = (q.Vp / q.BM) * ckl::lse_groups_per_tile(q.in_bf16);
   return q;
 }
 
@@ -225,6 +255,34 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   return w;
 }
 
+struct FusedWs {
+  size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, s, Ht, Wt, G, Gt, mtab, dHp, dW, total;
+};
+FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
+  FusedWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+  w.idx_s = take(q.T * q.K * 4);
+  w.p_s = take(q.T * q.K * 4);
+  w.zg_s = take(q.T * q.K * 4);
+  w.E = take(q.T * 4);
+  w.M = take(q.T * 4);
+  w.part = take(q.c_splits * q.Cs * 8);
+  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.N = take(4);
+  w.bad = take(4);
+  w.s = take(q.Tp * 4);
+  w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
+  w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
+  w.G = take((size_t)q.Cs * (q.Vp + kLdPad) * q.esz);
+  w.Gt = take((size_t)q.Vp * (q.Cs + kLdPad) * q.esz);
+  w.mtab = take((size_t)q.groups * q.Cs * 4);
+  w.dHp = take((size_t)q.Sh * q.Cs * q.d * 4);
+  w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
+  w.total = o;
+  return w;
+}
+
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 ckl_status check_validate_flag(int* bad_dev, hipStream_t st) {
@@ -243,9 +301,10 @@ ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
   if (!bytes) return fail(CKL_ERR_INVALID_ARG, "bytes is NULL");
-  if (which != 0 && which != 1) return fail(CKL_ERR_INVALID_ARG, "which must be 0 (forward) or 1 (backward)");
+  if (which < 0 || which > 2)
+    return fail(CKL_ERR_INVALID_ARG, "which must be 0 (forward), 1 (backward) or 2 (forward + backward)");
   const Plan q = make_plan(p);
-  *bytes = which == 0 ? fwd_layout(q).total : bwd_layout(q, p).total;
+  *bytes = which == 0 ? fwd_layout(q).total : which == 1 ? bwd_layout(q, p).total : fused_layout(q, p).total;
   return CKL_OK;
 }
 
@@ -289,7 +348,7 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                 [&] {
                   return ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits,
-                                             (int)q.f_tps, st);
+                                             (int)q.f_tps, nullptr, 0, nullptr, 0, st);
                 }),
           "fwd_lse");
   HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
@@ -392,6 +451,136 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   if (p->dw_dtype == CKL_BF16)
     HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),
             "cast dW");
+  return CKL_OK;
+}
+
+ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void* W, const int32_t* idx,
+                                const float* tlogit, const uint8_t* mask, const float* grad_loss, float* loss,
+                                float* lse, float* row_loss, void* dH, void* dW, void* ws, size_t ws_bytes,
+                                void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!H || !W || !idx || !tlogit || !loss || !lse || !dH || !dW)
+    return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(dH) || !aligned16(dW) ||
+      !aligned16(ws))
+    return fail(CKL_ERR_INVALID_ARG, "H, W, idx, tlogit, dH, dW and ws must be 16-byte aligned");
+  if (((uintptr_t)loss & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)row_loss & 3u) || ((uintptr_t)grad_loss & 3u))
+    return fail(CKL_ERR_INVALID_ARG, "loss, lse, row_loss and grad_loss must be 4-byte aligned");
+  const Plan q = make_plan(p);
+  const FusedWs w = fused_layout(q, p);
+  if (!ws || ws_bytes < w.total)
+    return fail(CKL_ERR_WORKSPACE, "forward + backward workspace needs %zu bytes, got %zu", w.total,
+                ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* b = (char*)ws;
+  int* idx_s = (int*)(b + w.idx_s);
+  float* p_s = (float*)(b + w.p_s);
+  float* zg_s = (float*)(b + w.zg_s);
+  float* E = (float*)(b + w.E);
+  float* M = (float*)(b + w.M);
+  double* blk = (double*)(b + w.blk);
+  int* N = (int*)(b + w.N);
+  int* bad = (int*)(b + w.bad);
+  float* srow = (float*)(b + w.s);
+  char* Ht = b + w.Ht;
+  char* Wt = b + w.Wt;
+  char* G = b + w.G;
+  char* Gt = b + w.Gt;
+  float* mtab = (float*)(b + w.mtab);
+  float* dHp = (float*)(b + w.dHp);
+  float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
+  const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
+  const int64_t ldG = q.Vp + kLdPad, ldGt = q.Cs + kLdPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
+
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
+  HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
+                [&] {
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
+                                                  p->validate ? bad : nullptr, st);
+                }),
+          "teacher_prep");
+  if (p->validate) {
+    s = check_validate_flag(bad, st);
+    if (s != CKL_OK) return s;
+  }
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st); }),
+          "row_scale");
+  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, ldH, st); }),
+          "transpose H");
+  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, ldW, st); }),
+          "transpose W");
+
+  for (int64_t c = 0; c < q.nS; ++c) {
+    const int64_t tb0 = c * q.Cs;
+    const int rows = (int)std::min(q.Cs, q.T - tb0);           // real rows of the chunk
+    const int rows_p = (int)std::min(q.Cs, q.Tp - tb0);        // whole logit tiles
+    const char* Hc = (const char*)H + tb0 * q.d * q.esz;
+    HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
+                  [&] {
+                    return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, G, ldG, mtab, q.Cs, st);
+                  }),
+            "fwd_lse (store)");
+    HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                  [&] {
+                    return ckl::launch_fwd_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K, zg_s + tb0 * K,
+                                                E + tb0, M + tb0, mask ? mask + tb0 : nullptr, lse + tb0,
+                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0 / 256, st);
+                  }),
+            "fwd_rows");
+    HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
+                  [&] {
+                    return ckl::launch_gpass(q.in_bf16, G, ldG, Gt, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
+                                             rows, rows_p, V, (int)q.Vp, st);
+                  }),
+            "gpass");
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                  [&] {
+                    return ckl::launch_gfix(q.in_bf16, rows, K, V, idx_s + tb0 * K, p_s + tb0 * K, zg_s + tb0 * K,
+                                            srow + tb0, M + tb0, lse + tb0, G, ldG, Gt, ldGt, st);
+                  }),
+            "gfix");
+    // dH rows of the chunk as Sh split-k partials (long k: scheduled first),
+    // dW (+)= G^T H_chunk
+    ckl::GemmArgs gdh{G, ldG, Wt, ldW, dHp, q.d, rows, d, (int)q.Vs, 0};
+    gdh.batches = (int)q.Sh;
+    gdh.kdim_last = (int)(q.Vp - (q.Sh - 1) * q.Vs);
+    gdh.xb = q.Vs;
+    gdh.yb = q.Vs;
+    gdh.ob = q.Cs * q.d;
+    const ckl::GemmArgs gdw{Gt, ldGt, Ht + tb0 * q.esz, ldH, dWacc, q.d, V, d, rows_p, c > 0};
+    HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdh, gdw, st); }),
+            "gemm dH parts + dW");
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                  [&] {
+                    return ckl::launch_splitk_sum(dHp, q.Cs * q.d, (int)q.Sh, (int64_t)rows * q.d,
+                                                  (char*)dH + tb0 * q.d * (p->dh_dtype == CKL_BF16 ? 2 : 4),
+                                                  p->dh_dtype == CKL_BF16, st);
+                  }),
+            "dH sum");
+  }
+  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                [&] { return ckl::launch_loss_reduce(blk, (int)ceil_div(q.T, 256), N, loss, st); }),
+          "loss_reduce");
+  if (p->dw_dtype == CKL_BF16)
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),
+            "cast dW");
+  return CKL_OK;
+}
+
+ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!out) return fail(CKL_ERR_INVALID_ARG, "out is NULL");
+  const Plan q = make_plan(p);
+  out[0] = q.Cs;
+  out[1] = q.nS;
+  out[2] = q.Sh;
+  out[3] = q.Vs;
   return CKL_OK;
 }
 

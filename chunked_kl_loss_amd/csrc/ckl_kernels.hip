@@ -18,6 +18,8 @@
 //   gemm_store     dH (+)= G W and dW (+)= G^T H on the same MFMA main loop
 #include "ckl_kernels.hpp"
 
+#include <type_traits>
+
 #include "ckl_tile.hpp"
 
 namespace ckl {
@@ -185,13 +187,22 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
 // tiles_per_split tiles of BM rows), n_tblocks x n_splits in all, laid out
 // XCD-aware (kGroupT token blocks per group).  Output part[split * T + t] =
 // (m, s): the base-2 log-sum-exp state of row t over the split.
+//
+// STORE (the fused forward + backward): the exponentials the running sum is
+// built from are also kept.  Every lane owns, per token, the vocabulary rows
+// of one (wave_m, lane >> 5) group of each tile and a running maximum m over
+// them (base 2).  It stores u = 2^(z log2e - m) <= 1 at G[t][v] (zero for
+// v >= V) and m itself at mtab[((vt WAVES_M + wave_m) 2 + (lane >> 5)) ldm + t],
+// so that exp(z - LSE) = u 2^(m - LSE log2e) can be formed once the LSE is
+// known, without recomputing z.  No overflow: u <= 1 and m <= LSE log2e.
 constexpr int kGroupT = 8;
 
-template <class C>
+template <class C, bool STORE>
 __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
     const int* __restrict__ idx_s, float* __restrict__ zg_s, float2* __restrict__ part, int n_vtiles,
-    int tiles_per_split, int n_tblocks, int n_splits) {
+    int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
+    float* __restrict__ mtab, int64_t ldm) {
   using TIn = typename C::TIn;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
@@ -237,18 +248,6 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
           if (v < V) mx = fmaxf(mx, tile.acc[mb][nb][r] * kLog2e);
         }
       const float mn = fmaxf(rm[nb], mx);
-      float ssum = 0.f;
-      if (mn != -INFINITY) {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = vbase + mb * 32 + acc_row(r, lane);
-            if (v < V) ssum += fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn);
-          }
-        rs[nb] = rs[nb] * fast_exp2(rm[nb] - mn) + ssum;
-        rm[nb] = mn;
-      }
       // logits at the teacher indices of this row that fall in this tile
       while (nxt[nb] < vend) {
         const int vl = nxt[nb] - vbase;
@@ -264,6 +263,37 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
         }
         ++cur[nb];
         nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok[nb] * K + cur[nb]] : kIdxEnd;
+      }
+      float ssum = 0.f;
+      if (mn != -INFINITY) {
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + mb * 32 + acc_row(r, lane);
+            const float u = v < V ? fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn) : 0.f;
+            ssum += u;
+            if constexpr (STORE) tile.acc[mb][nb][r] = u;
+          }
+        rs[nb] = rs[nb] * fast_exp2(rm[nb] - mn) + ssum;
+        rm[nb] = mn;
+      } else if constexpr (STORE) {
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
+      }
+      if constexpr (STORE) {
+        const int64_t trow = tok[nb];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int vcol = vbase + mb * 32 + 8 * i + 4 * (lane >> 5);
+            store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
+                        tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
+          }
+        mtab[(((int64_t)vt * C::WAVES_M + wave_m) * 2 + (lane >> 5)) * ldm + trow] = mn;
       }
     }
   }
@@ -491,11 +521,142 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   }
 }
 
+// ------------------------------------------------ fused G formation (gpass) --
+// The fused forward + backward keeps u = 2^(z log2e - m) of every logit of a
+// row chunk in G (see fwd_lse_kernel).  Once the chunk's LSE is known, one
+// 128 x 128 (token x vocabulary) tile per block turns u into
+//   g = s_t M_t u 2^(m - LSE_t log2e)  ( = s_t M_t exp(z - LSE_t) )
+// in place and writes the transpose G^T through LDS; HBM traffic 3 elements
+// per entry.  The teacher columns are corrected afterwards (gfix_kernel).
+template <typename TIn>
+__global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t ldG, TIn* __restrict__ Gt,
+                                                    int64_t ldGt, const float* __restrict__ mtab, int64_t ldm,
+                                                    const float* __restrict__ srow, const float* __restrict__ Mrow,
+                                                    const float* __restrict__ lse, int rows, int V, int tile_m,
+                                                    int wave_rows) {
+  constexpr bool kBF16 = sizeof(TIn) == 2;
+  constexpr int E = 16 / (int)sizeof(TIn);  // entries per 16-byte chunk
+  constexpr int CPR = 128 / E;              // chunks per 128-entry row
+  constexpr int RPP = 256 / CPR;            // rows per pass of the block
+  constexpr int LDT = kBF16 ? 130 : 129;    // LDS row stride (elements)
+  using TS = typename std::conditional<kBF16, uint16_t, float>::type;
+  __shared__ TS tr[128 * LDT];  // tr[v_local][t_local]
+  const int t0 = blockIdx.y * 128, v0 = blockIdx.x * 128;
+  const int c = threadIdx.x % CPR, rr = threadIdx.x / CPR;
+  const int vc = v0 + c * E;  // first vocabulary entry of this thread's chunks
+  // all E entries of a chunk share the tile and the wave row block; entries
+  // with bit 2 of v clear / set belong to lane groups h = 0 / 1
+  const int64_t grp = ((int64_t)(vc / tile_m) * (tile_m / wave_rows) + (vc % tile_m) / wave_rows) * 2;
+  for (int i = rr; i < 128; i += RPP) {
+    const int t = t0 + i;
+    float f0 = 0.f, f1 = 0.f;
+    bool ok = false;
+    if (t < rows) {
+      const float sc = srow[t];
+      if (sc != 0.f) {
+        ok = true;
+        const float coef = sc * Mrow[t];
+        const float l2 = lse[t] * kLog2e;
+        f0 = coef * fast_exp2(mtab[grp * ldm + t] - l2);
+        f1 = coef * fast_exp2(mtab[(grp + 1) * ldm + t] - l2);
+      }
+    }
+    TIn* gp = G + (int64_t)t * ldG + vc;
+    float g[E];
+    if constexpr (kBF16) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(gp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float u = bf16_bits_to_f32((x[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        g[e] = (ok && vc + e < V) ? u * (((vc + e) & 4) ? f1 : f0) : 0.f;
+      }
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < E; e += 2) y[e >> 1] = pack_bf16x2(g[e], g[e + 1]);
+      *reinterpret_cast<u32x4*>(gp) = y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = (uint16_t)((y[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[e] = (ok && vc + e < V) ? x[e] * (((vc + e) & 4) ? f1 : f0) : 0.f;
+      f32x4 y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = g[e];
+      *reinterpret_cast<f32x4*>(gp) = y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = g[e];
+    }
+  }
+  __syncthreads();
+  for (int i = rr; i < 128; i += RPP) {  // vocabulary row v0 + i, tokens t0 + c E ..
+    TIn* dst = Gt + (int64_t)(v0 + i) * ldGt + t0 + c * E;
+    const TS* src = tr + i * LDT + c * E;
+    if constexpr (kBF16) {
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < E; e += 2) y[e >> 1] = (uint32_t)src[e] | ((uint32_t)src[e + 1] << 16);
+      *reinterpret_cast<u32x4*>(dst) = y;
+    } else {
+      f32x4 y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = src[e];
+      *reinterpret_cast<f32x4*>(dst) = y;
+    }
+  }
+}
+
+// Teacher columns: g = s_t (M_t 2^(zg log2e - LSE_t log2e) - p), the same
+// fp32 expression the recomputing backward evaluates, rounded once.
+template <typename TIn>
+__global__ __launch_bounds__(256) void gfix_kernel(int rows, int K, int V, const int* __restrict__ idx_s,
+                                                   const float* __restrict__ p_s, const float* __restrict__ zg_s,
+                                                   const float* __restrict__ srow, const float* __restrict__ Mrow,
+                                                   const float* __restrict__ lse, TIn* __restrict__ G, int64_t ldG,
+                                                   TIn* __restrict__ Gt, int64_t ldGt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * K) return;
+  const int t = (int)(i / K);
+  const float sc = srow[t];
+  if (sc == 0.f) return;  // the row is already zero
+  const int v = idx_s[i];
+  if (v < 0 || v >= V) return;  // unchecked bad index: matches no column
+  const float coef = sc * Mrow[t];
+  const float g = coef * fast_exp2(zg_s[i] * kLog2e - lse[t] * kLog2e) - sc * p_s[i];
+  if constexpr (sizeof(TIn) == 2) {
+    const uint16_t b = (uint16_t)f32_to_bf16_bits(g);
+    reinterpret_cast<uint16_t*>(G)[(int64_t)t * ldG + v] = b;
+    reinterpret_cast<uint16_t*>(Gt)[(int64_t)v * ldGt + t] = b;
+  } else {
+    G[(int64_t)t * ldG + v] = g;
+    Gt[(int64_t)v * ldGt + t] = g;
+  }
+}
+
+// out[i] = part[i] + part[pstride + i] + ... (S terms, this order), 4 per thread.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int64_t pstride, int S,
+                                                         int64_t n4, void* __restrict__ out, int out_bf16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
+  for (int s = 1; s < S; ++s) a += reinterpret_cast<const f32x4*>(part + s * pstride)[i];
+  if (out_bf16)
+    store4<bf16_t>(reinterpret_cast<bf16_t*>(out) + 4 * i, a[0], a[1], a[2], a[3]);
+  else
+    reinterpret_cast<f32x4*>(out)[i] = a;
+}
+
 // ------------------------------------------------------ plain contraction --
 // out[m, n] (+)= sum_k X[m, k] Y[n, k] for m < M, n < N (fp32 out).  Two
 // independent problems share one launch (the dH and dW products of a G
-// block): workgroups [0, p0.tiles) take problem 0, the rest problem 1, so the
-// tail of one fills the machine with tiles of the other.
+// block): workgroups [0, p0.tiles) take problem 0, the rest problem 1 (each
+// spread over the XCDs separately), so the tail of one fills the machine with
+// tiles of the other.
+//
+// A problem may be a batch of `batches` products of the same shape whose
+// operands and outputs sit xb, yb and ob elements apart, the last one with
+// k extent kdim_last (split-k over a long contraction: each split writes its
+// own partial output, summed later in a fixed order).
 template <typename TIn>
 struct GemmProblem {
   const TIn* X;
@@ -505,7 +666,9 @@ struct GemmProblem {
   float* out;
   int64_t ldo;
   int M, N, kdim, beta;
-  int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN)
+  int batches, kdim_last;
+  int64_t xb, yb, ob;
+  int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN) * batches
 };
 
 constexpr int kGroupM = 4;
@@ -518,19 +681,39 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
   const int wave = threadIdx.x >> 6;
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
-  int bid = xcd_remap(blockIdx.x, p0.tiles + p1.tiles);
-  const bool second = bid >= p0.tiles;  // workgroup-uniform
-  if (second) bid -= p0.tiles;
+  // Each problem is spread over all XCDs on its own (problem 1 starts at a
+  // multiple of 8 workgroups, so w % 8 still names the XCD): remapping the
+  // two together would put the first problem's tiles, often the long ones,
+  // on the first XCDs only.
+  const int n0p = (p0.tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  int bid = blockIdx.x;
+  const bool second = bid >= n0p;  // workgroup-uniform
+  if (!second) {
+    bid = xcd_remap(bid, n0p);
+    if (bid >= p0.tiles) return;  // padding workgroup
+  } else {
+    bid = xcd_remap(bid - n0p, p1.tiles);
+  }
   // field-wise selection keeps the by-value kernel arguments in registers
   const typename C::TIn* X = second ? p1.X : p0.X;
   const typename C::TIn* Y = second ? p1.Y : p0.Y;
   float* out = second ? p1.out : p0.out;
   const int64_t ldx = second ? p1.ldx : p0.ldx, ldy = second ? p1.ldy : p0.ldy, ldo = second ? p1.ldo : p0.ldo;
-  const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, kdim = second ? p1.kdim : p0.kdim;
+  const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, kdim_all = second ? p1.kdim : p0.kdim;
   const int beta = second ? p1.beta : p0.beta;
   const int tiles_m = second ? p1.tiles_m : p0.tiles_m, tiles = second ? p1.tiles : p0.tiles;
+  const int batches = second ? p1.batches : p0.batches;
+  const int per_batch = tiles / batches;
+  const int bt = bid / per_batch;
+  bid -= bt * per_batch;
+  if (bt > 0) {
+    X += bt * (second ? p1.xb : p0.xb);
+    Y += bt * (second ? p1.yb : p0.yb);
+    out += bt * (second ? p1.ob : p0.ob);
+  }
+  const int kdim = bt == batches - 1 ? (second ? p1.kdim_last : p0.kdim_last) : kdim_all;
   int tm, tn;
-  grouped_mn(bid, tiles_m, tiles / tiles_m, kGroupM, tm, tn);
+  grouped_mn(bid, tiles_m, per_batch / tiles_m, kGroupM, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   typename C::TileT tile;
   run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
@@ -612,33 +795,55 @@ hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K
 
 template <typename TIn>
 static hipError_t fwd_lse_t(const void* H, const void* W, int T, int d, int V, int K, const int* idx_s, float* zg_s,
-                            void* part, int n_splits, int tiles_per_split, hipStream_t st) {
+                            void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG, float* mtab,
+                            int64_t ldm, hipStream_t st) {
   using C = typename CfgOf<TIn>::type;
   const int n_vtiles = (V + C::BM - 1) / C::BM;
   const int n_tblocks = (T + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL(fwd_lse_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,
-                     (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles, tiles_per_split, n_tblocks,
-                     n_splits);
+  if (G)
+    hipLaunchKernelGGL((fwd_lse_kernel<C, true>), dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st,
+                       (const TIn*)H, (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles,
+                       tiles_per_split, n_tblocks, n_splits, (TIn*)G, ldG, mtab, ldm);
+  else
+    hipLaunchKernelGGL((fwd_lse_kernel<C, false>), dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st,
+                       (const TIn*)H, (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles,
+                       tiles_per_split, n_tblocks, n_splits, (TIn*)nullptr, (int64_t)0, (float*)nullptr,
+                       (int64_t)0);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
 hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
-                          float* zg_s, void* part, int n_splits, int tiles_per_split, hipStream_t st) {
-  return in_bf16 ? fwd_lse_t<bf16_t>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, st)
-                 : fwd_lse_t<float>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, st);
+                          float* zg_s, void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG,
+                          float* mtab, int64_t ldm, hipStream_t st) {
+  return in_bf16 ? fwd_lse_t<bf16_t>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, G, ldG, mtab,
+                                     ldm, st)
+                 : fwd_lse_t<float>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, G, ldG, mtab,
+                                    ldm, st);
+}
+
+hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
+                           const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
+                           double* blk_sum, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(256), 0, st, (const float2*)part, S, T, K, p_s, zg_s, Erow,
+                     Mrow, mask, lse, row_loss, blk_sum);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_loss_reduce(const double* blk_sum, int nblk, const int* N, float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, blk_sum, nblk, N, loss);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
 }
 
 hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
                                float* row_loss, double* blk_sum, const int* N, float* loss, hipStream_t st) {
-  const int nblk = (T + 255) / 256;
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(256), 0, st, (const float2*)part, S, T, K, p_s, zg_s, Erow,
-                     Mrow, mask, lse, row_loss, blk_sum);
-  CKL_LAUNCH_CHECK();
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, blk_sum, nblk, N, loss);
-  CKL_LAUNCH_CHECK();
-  return hipSuccess;
+  hipError_t e = launch_fwd_rows(part, S, T, K, p_s, zg_s, Erow, Mrow, mask, lse, row_loss, blk_sum, st);
+  if (e != hipSuccess) return e;
+  return launch_loss_reduce(blk_sum, (T + 255) / 256, N, loss, st);
 }
 
 hipError_t launch_transpose_pad(int in_bf16, const void* src, int R, int C, int Rp, void* dst, int64_t ldd,
@@ -702,11 +907,16 @@ static hipError_t gemm_pair_t(const GemmArgs& a0, const GemmArgs& a1, hipStream_
     p[i].N = a[i]->N;
     p[i].kdim = a[i]->kdim;
     p[i].beta = a[i]->beta;
+    p[i].batches = a[i]->batches > 0 ? a[i]->batches : 1;
+    p[i].kdim_last = a[i]->batches > 1 ? a[i]->kdim_last : a[i]->kdim;
+    p[i].xb = a[i]->xb;
+    p[i].yb = a[i]->yb;
+    p[i].ob = a[i]->ob;
     p[i].tiles_m = a[i]->M > 0 ? (a[i]->M + C::BM - 1) / C::BM : 0;
-    p[i].tiles = a[i]->M > 0 && a[i]->N > 0 ? p[i].tiles_m * ((a[i]->N + C::BN - 1) / C::BN) : 0;
+    p[i].tiles = a[i]->M > 0 && a[i]->N > 0 ? p[i].tiles_m * ((a[i]->N + C::BN - 1) / C::BN) * p[i].batches : 0;
   }
-  const int n = p[0].tiles + p[1].tiles;
-  if (n == 0) return hipSuccess;
+  if (p[0].tiles + p[1].tiles == 0) return hipSuccess;
+  const int n = (p[0].tiles + kNumXcd - 1) / kNumXcd * kNumXcd + p[1].tiles;
   hipLaunchKernelGGL(gemm_store_kernel<C>, dim3(n), dim3(C::NTHREADS), 0, st, p[0], p[1]);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
@@ -716,7 +926,52 @@ hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1,
   return in_bf16 ? gemm_pair_t<bf16_t>(a0, a1, st) : gemm_pair_t<float>(a0, a1, st);
 }
 
+hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldGt, const float* mtab, int64_t ldm,
+                        const float* srow, const float* Mrow, const float* lse, int rows, int rows_p, int V, int Vp,
+                        hipStream_t st) {
+  if (rows_p % 128 || Vp % 128) return hipErrorInvalidValue;
+  const dim3 grid(Vp / 128, rows_p / 128);
+  if (in_bf16)
+    hipLaunchKernelGGL(gpass_kernel<bf16_t>, grid, dim3(256), 0, st, (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm,
+                       srow, Mrow, lse, rows, V, CfgBF16::BM, CfgBF16::WM);
+  else
+    hipLaunchKernelGGL(gpass_kernel<float>, grid, dim3(256), 0, st, (float*)G, ldG, (float*)Gt, ldGt, mtab, ldm, srow,
+                       Mrow, lse, rows, V, CfgF32::BM, CfgF32::WM);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gfix(int in_bf16, int rows, int K, int V, const int* idx_s, const float* p_s, const float* zg_s,
+                       const float* srow, const float* Mrow, const float* lse, void* G, int64_t ldG, void* Gt,
+                       int64_t ldGt, hipStream_t st) {
+  const int64_t n = (int64_t)rows * K;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (in_bf16)
+    hipLaunchKernelGGL(gfix_kernel<bf16_t>, grid, dim3(256), 0, st, rows, K, V, idx_s, p_s, zg_s, srow, Mrow, lse,
+                       (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt);
+  else
+    hipLaunchKernelGGL(gfix_kernel<float>, grid, dim3(256), 0, st, rows, K, V, idx_s, p_s, zg_s, srow, Mrow, lse,
+                       (float*)G, ldG, (float*)Gt, ldGt);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_splitk_sum(const float* part, int64_t pstride, int S, int64_t n, void* out, int out_bf16,
+                             hipStream_t st) {
+  if (n % 4 || pstride % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, pstride, S, n4,
+                     out, out_bf16);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
 int tile_rows_m(int in_bf16) { return in_bf16 ? CfgBF16::BM : CfgF32::BM; }
 int tile_rows_n(int in_bf16) { return in_bf16 ? CfgBF16::BN : CfgF32::BN; }
+int gemm_tile(int in_bf16) { return in_bf16 ? CfgBF16Gemm::BM : CfgF32::BM; }
+int lse_groups_per_tile(int in_bf16) { return in_bf16 ? 2 * CfgBF16::WAVES_M : 2 * CfgF32::WAVES_M; }
+static_assert(CfgBF16Gemm::BM == CfgBF16Gemm::BN && CfgF32::BM == CfgF32::BN, "square contraction tiles");
 
 }  // namespace ckl

@@ -13,11 +13,36 @@ hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const i
                             hipStream_t st);
 hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
                                float* Erow, float* Mrow, float* zg_s, int* bad, hipStream_t st);
+// G == nullptr: log-sum-exp partials only.  Otherwise also the exponentials
+// u (G, row stride ldG) and the per-tile maxima (mtab, row stride ldm) of the
+// fused forward + backward.
 hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
-                          float* zg_s, void* part, int n_splits, int tiles_per_split, hipStream_t st);
+                          float* zg_s, void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG,
+                          float* mtab, int64_t ldm, hipStream_t st);
+// Per-row LSE and loss plus per-256-row fp64 sums; then the mean over N.
+hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
+                           const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
+                           double* blk_sum, hipStream_t st);
+hipError_t launch_loss_reduce(const double* blk_sum, int nblk, const int* N, float* loss, hipStream_t st);
 hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
                                float* row_loss, double* blk_sum, const int* N, float* loss, hipStream_t st);
+// Fused path, after the rows' LSE is known: G[t][v] (holding u) becomes
+// g = s_t M_t u 2^(m - lse_t log2e) in place, zero for t >= rows, v >= V or
+// s_t = 0, and G^T[v][t] = g, over t < rows_p and v < Vp (tile multiples).
+hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldGt, const float* mtab, int64_t ldm,
+                        const float* srow, const float* Mrow, const float* lse, int rows, int rows_p, int V, int Vp,
+                        hipStream_t st);
+// Teacher columns of rows < rows: g = s_t (M_t exp(zg - lse_t) - p), from the
+// fp32 logits kept by the forward, into G and G^T (indices outside [0, V) are
+// skipped).
+hipError_t launch_gfix(int in_bf16, int rows, int K, int V, const int* idx_s, const float* p_s, const float* zg_s,
+                       const float* srow, const float* Mrow, const float* lse, void* G, int64_t ldG, void* Gt,
+                       int64_t ldGt, hipStream_t st);
+// out[i] = sum_{s < S} part[s * pstride + i] for i < n (fixed order), as fp32
+// or bf16.
+hipError_t launch_splitk_sum(const float* part, int64_t pstride, int S, int64_t n, void* out, int out_bf16,
+                             hipStream_t st);
 hipError_t launch_transpose_pad(int in_bf16, const void* src, int R, int C, int Rp, void* dst, int64_t ldd,
                                 hipStream_t st);
 hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
@@ -26,6 +51,8 @@ hipError_t launch_bwd_grad(int in_bf16, const void* H, const void* W, int T, int
                            int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G, int64_t ldG,
                            void* Gt, int64_t ldGt, hipStream_t st);
 // out[m, n] (+)= sum_k X[m, k] Y[n, k]; row-major operands contiguous in k.
+// batches > 1: that many products xb / yb / ob elements apart, the last with
+// k extent kdim_last.
 struct GemmArgs {
   const void* X;
   int64_t ldx;
@@ -34,6 +61,8 @@ struct GemmArgs {
   float* out;
   int64_t ldo;
   int M, N, kdim, beta;
+  int batches = 1, kdim_last = 0;
+  int64_t xb = 0, yb = 0, ob = 0;
 };
 // Two independent products in one launch (problem 0's tiles are scheduled first).
 hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1, hipStream_t st);
@@ -41,5 +70,8 @@ hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1,
 // Tile extents of the contraction kernels: G blocks are whole tiles.
 int tile_rows_m(int in_bf16);  // vocabulary rows per logit tile (BM)
 int tile_rows_n(int in_bf16);  // token rows per logit tile (BN)
+int gemm_tile(int in_bf16);    // square tile edge of the plain contraction
+// running-maximum groups per logit tile kept by the fused forward
+int lse_groups_per_tile(int in_bf16);
 
 }  // namespace ckl

@@ -90,9 +90,10 @@ typedef struct {
                      /* undefined, as it is for repeated entries.          */
 } ckl_problem;
 
-/* Workspace bytes needed by ckl_forward (which = 0) or ckl_backward
- * (which = 1) for problem *p.  Writes *bytes; returns CKL_OK or
- * CKL_ERR_INVALID_ARG / CKL_ERR_UNSUPPORTED for a bad problem. */
+/* Workspace bytes needed by ckl_forward (which = 0), ckl_backward
+ * (which = 1) or ckl_forward_backward (which = 2) for problem *p.  Writes
+ * *bytes; returns CKL_OK or CKL_ERR_INVALID_ARG / CKL_ERR_UNSUPPORTED for a
+ * bad problem. */
 ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes);
 
 /* Forward pass: loss, per-row log-sum-exp and per-row KL.
@@ -131,6 +132,43 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
  * Host-only; touches no device. */
 ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
 
+/* Forward and backward in one call, without recomputing the logits.
+ *
+ * The README page above lists a Forward-Chunked Loss that keeps the student
+ * logits for the backward pass (the fastest variant in the article "A KL loss
+ * tweak lets a single GPU distill a 120B model without melting") and the Full
+ * Chunked KL that bounds memory by recomputing them.  This call keeps the
+ * logits of one row chunk at a time: memory stays bounded by `chunk` and
+ * nothing is recomputed.  For each chunk of rows the logit tiles are
+ * multiplied once; besides the online log-sum-exp of ckl_forward the kernel
+ * stores u = exp(z - m) in in_dtype, where m is a running maximum kept per
+ * group of vocabulary rows (so u <= 1 and nothing overflows).  When the
+ * chunk's LSE is known, u becomes G = s_t M_t u exp(m - LSE_t) in place, the
+ * K teacher columns are recomputed in fp32 from the logits kept at the
+ * teacher indices, and dW += G^T H_chunk, dH_chunk = G W follow (dH as a
+ * split-k product summed in a fixed order).
+ *
+ * Arguments as in ckl_forward and ckl_backward; grad_loss ([1] device
+ * float32 or NULL = 1) must hold its value when the call's kernels run.
+ * loss, lse and row_loss agree with ckl_forward up to the order of the split
+ * merges (float rounding); dH and dW agree with ckl_backward up to one more
+ * rounding of the non-teacher entries of G to in_dtype (u is rounded before
+ * it is rescaled).
+ *   ws: device workspace of at least ckl_workspace_size(p, 2) bytes: two
+ *   chunk x V buffers of in_dtype (G and its transpose), H^T and W^T, the
+ *   dH split-k partials and small per-row arrays.
+ * Rows per chunk: `chunk` rounded up to whole tiles (256 rows for bf16,
+ * 128 for fp32), at most T rounded up. */
+ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void* W,
+                                const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                                const float* grad_loss, float* loss, float* lse, float* row_loss,
+                                void* dH, void* dW, void* ws, size_t ws_bytes, void* stream);
+
+/* The chunk plan ckl_forward_backward uses for problem *p: out[0] = rows per
+ * chunk, out[1] = number of chunks, out[2] = number of dH split-k parts,
+ * out[3] = vocabulary columns per part.  Host-only; touches no device. */
+ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]);
+
 /* Kernel classes for the timing records below. */
 typedef enum {
   CKL_KERNEL_TEACHER_PREP = 0, /* teacher softmax + sort                      */
@@ -138,7 +176,7 @@ typedef enum {
   CKL_KERNEL_FWD_FINALIZE = 2, /* split merge, row loss, masked mean          */
   CKL_KERNEL_BWD_GRAD = 3,     /* backward logit recompute + G epilogue       */
   CKL_KERNEL_GEMM_DHDW = 4,    /* dW (+)= G^T H and dH (+)= G W, one launch   */
-  CKL_KERNEL_RESERVED5 = 5,    /* unused                                      */
+  CKL_KERNEL_G_PASS = 5,       /* fused call: u -> G in place, G^T          */
   CKL_KERNEL_TRANSPOSE = 6,    /* H^T and W^T staging                         */
   CKL_KERNEL_OTHER = 7,        /* counts, scales, fills, casts               */
   CKL_KERNEL_CLASSES = 8

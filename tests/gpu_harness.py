@@ -59,6 +59,26 @@ def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="in
     return out
 
 
+def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False):
+    """The one-call forward + backward (no logit recompute) through the C ABI."""
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    H, W, idx, tl, m = to_device(x)
+    if not isinstance(mask, str):
+        m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=np.uint8)).cuda()
+    chunk = x.chunk if chunk is None else chunk
+    g = None if grad_loss is None else torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
+    loss, lse, row_loss, dH, dW = ckl.forward_backward(H, W, idx, tl, m, g, chunk=chunk, dh_dtype=dh_dtype,
+                                                       dw_dtype=dw_dtype, validate=validate, want_row_loss=True)
+    torch.cuda.synchronize()
+    out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy(),
+               dH=dH.double().cpu().numpy(), dW=dW.double().cpu().numpy())
+    del H, W, idx, tl, m, dH, dW
+    torch.cuda.empty_cache()
+    return out
+
+
 def max_rel(got, ref):
     """max |got - ref| / max |ref| (the gradient criterion)."""
     scale = np.abs(ref).max()

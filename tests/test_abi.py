@@ -68,9 +68,9 @@ def test_problem_validation(lib, kw, status):
 
 def test_workspace_query_and_plan(lib):
     p = _prob()
-    assert B.workspace_size(p, 0) > 0 and B.workspace_size(p, 1) > 0
+    assert B.workspace_size(p, 0) > 0 and B.workspace_size(p, 1) > 0 and B.workspace_size(p, 2) > 0
     with pytest.raises(B.CklError):
-        B.workspace_size(p, 2)
+        B.workspace_size(p, 3)
     plan = B.backward_plan(p)
     assert plan["Tc"] % 128 == 0 and plan["Vc"] % 128 == 0  # fp32 tiles are 128 x 128
     assert plan["nT"] * plan["Tc"] >= 256 and plan["nV"] * plan["Vc"] >= 2048
@@ -87,6 +87,13 @@ def test_null_and_alignment_rejected(lib):
     assert st == B.CKL_ERR_INVALID_ARG
     st = lib.ckl_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, None, None, fake, fake, 1 << 30, None)
     assert st == B.CKL_ERR_INVALID_ARG
+    # fused call: dW missing, then a misaligned lse
+    st = lib.ckl_forward_backward(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, None, fake, None,
+                                  fake, 1 << 30, None)
+    assert st == B.CKL_ERR_INVALID_ARG
+    st = lib.ckl_forward_backward(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake + 2, None, fake,
+                                  fake, fake, 1 << 30, None)
+    assert st == B.CKL_ERR_INVALID_ARG
 
 
 def test_workspace_too_small_rejected(lib):
@@ -100,6 +107,10 @@ def test_workspace_too_small_rejected(lib):
     needb = B.workspace_size(p, 1)
     st = lib.ckl_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, None, fake, fake, fake, needb - 1,
                           None)
+    assert st == B.CKL_ERR_WORKSPACE
+    needf = B.workspace_size(p, 2)
+    st = lib.ckl_forward_backward(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, None, fake, fake,
+                                  fake, needf - 1, None)
     assert st == B.CKL_ERR_WORKSPACE
 
 
@@ -125,3 +136,26 @@ def test_plan_respects_budget(lib):
         assert q["Tc"] % tile == 0 and q["Vc"] % tile == 0
         assert q["n_buffers"] * q["Tc"] * q["Vc"] <= max(chunk * V // 2, tile * tile) or q["Tc"] == tile
         assert q["nT"] * q["Tc"] >= T and q["nV"] * q["Vc"] >= V
+
+
+def test_fused_plan_and_workspace(lib):
+    # chunks: `chunk` rounded up to 256 rows, covering every row; the dH
+    # split-k parts cover the padded vocabulary in 256-multiples
+    for T, V, chunk in [(32768, 201088, 2048), (262144, 201088, 512), (4096, 32000, 1024), (257, 2048, 64),
+                        (1000, 1000, 100000)]:
+        prob = B.make_problem(T, 2880, V, 100, chunk)
+        f = B.fused_plan(prob)
+        assert f["rows"] % 256 == 0 and f["rows"] >= min(chunk, T)
+        assert f["rows"] <= max(256, -(-chunk // 256) * 256)
+        assert f["chunks"] * f["rows"] >= T and (f["chunks"] - 1) * f["rows"] < T
+        Vp = -(-V // 256) * 256
+        assert f["part_cols"] % 256 == 0 and f["dh_parts"] * f["part_cols"] >= Vp
+        assert (f["dh_parts"] - 1) * f["part_cols"] < Vp
+    # the chunk buffers (G and G^T of rows x V, bf16) are the only part that
+    # scales with chunk; the rest grows linearly in T
+    def ws(T, chunk):
+        return B.workspace_size(B.make_problem(T, 2880, 201088, 100, chunk), 2)
+    a, b, c = ws(32768, 2048), ws(65536, 2048), ws(131072, 2048)
+    assert c - b == pytest.approx(2 * (b - a), rel=1e-3)
+    g2k, g4k = ws(32768, 2048), ws(32768, 4096)
+    assert g4k - g2k == pytest.approx(2 * 2048 * (201088 + 128) * 2, rel=0.05)

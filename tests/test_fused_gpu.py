@@ -1,0 +1,173 @@
+"""GPU parity of the one-call forward + backward (ckl_forward_backward: each
+row chunk's logits are multiplied once and kept as exp(z - m) in the
+workspace instead of being recomputed) against the fp64 oracle, element by
+element, on the problems of the two-call tests: the tiny fp32 workload, the
+4K x 32K bf16 workload, ragged reduced-row slices of the 201,088-vocabulary
+workloads (one with packed-document masks), chunk sizes that give one or
+many row chunks with a ragged last one, edge shapes and masks.
+
+Tolerances as for the two-call path (bf16 inputs: loss 2e-3 relative, dH / dW
+max-abs 1e-2 of max|ref|; fp32 inputs: 1e-5), which the extra rounding of
+exp(z - m) to bf16 (one bf16 ulp, 2^-8 relative at most, on each non-teacher
+entry of G before it is rescaled) stays well inside.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_inputs
+from tests.gpu_harness import TOL, max_rel, run_gpu, run_gpu_fused, say
+from tests.test_parity_gpu import _custom, check_full, oracle_full
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def inputs(cfg, seed=0, T=None):
+    key = (cfg, seed, T)
+    if key not in _cache:
+        _cache[key] = make_inputs(cfg, seed=seed, T=T)
+    return _cache[key]
+
+
+def test_fused_tiny_fp32_full():
+    x = inputs(0)
+    say(f"case fused tiny fp32 T={x.T} d={x.d} V={x.V} K={x.K} chunk={x.chunk}")
+    got = run_gpu_fused(x)
+    e = check_full(x, got, oracle_full(x), TOL["f32"], 1e-5)
+    say(f"  dH rel {e[0]:.2e} dW rel {e[1]:.2e}")
+
+
+def test_fused_small_bf16_full():
+    x = inputs(1)
+    say(f"case fused small bf16 T={x.T} d={x.d} V={x.V} K={x.K} chunk={x.chunk}")
+    got = run_gpu_fused(x)
+    e = check_full(x, got, oracle_full(x), TOL["bf16"], 2e-3)
+    say(f"  dH rel {e[0]:.2e} dW rel {e[1]:.2e}")
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 1000), (3, 677), (4, 677)])
+def test_fused_large_vocab_row_slices(cfg, T):
+    x = inputs(cfg, T=T)
+    say(f"case fused cfg{cfg} slice T={x.T} chunk={x.chunk} masked={x.mask is not None}")
+    got = run_gpu_fused(x)
+    e = check_full(x, got, oracle_full(x), TOL["bf16"], 2e-3)
+    say(f"  dH rel {e[0]:.2e} dW rel {e[1]:.2e}")
+
+
+@pytest.mark.parametrize("chunk", [1, 300, 513, 100000])
+def test_fused_chunk_sizes(chunk):
+    # 256-row chunks (1 -> 4 chunks, the last ragged), 512 and 768 rows, one chunk
+    import chunked_kl_loss_amd as ckl
+    x = inputs(1, T=1000)
+    plan = ckl.fused_plan(ckl.make_problem(x.T, x.d, x.V, x.K, chunk))
+    say(f"case fused chunk={chunk} T={x.T} plan={plan}")
+    got = run_gpu_fused(x, chunk=chunk, grad_loss=0.75)
+    check_full(x, got, oracle_full(x, grad_loss=0.75), TOL["bf16"], 2e-3)
+
+
+@pytest.mark.parametrize("T,d,V,K,dtype", [
+    (1, 8, 16, 1, "bf16"),
+    (3, 8, 1000, 7, "f32"),
+    (130, 24, 300, 300, "bf16"),
+    (257, 136, 129, 5, "bf16"),
+    (64, 4096, 4096, 64, "bf16"),
+    (300, 40, 777, 13, "f32"),
+])
+def test_fused_edge_shapes(T, d, V, K, dtype):
+    x = _custom(T, d, V, K, dtype)
+    say(f"case fused edge T={T} d={d} V={V} K={K} {dtype}")
+    got = run_gpu_fused(x, chunk=3, grad_loss=1.5)
+    check_full(x, got, oracle_full(x, grad_loss=1.5), TOL[dtype], 2e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_fused_masks_all_and_one():
+    x = _custom(200, 64, 700, 9)
+    say("case fused all rows masked")
+    got = run_gpu_fused(x, mask=np.zeros(200, np.uint8))
+    assert got["loss"] == 0.0
+    assert (got["dH"] == 0).all() and (got["dW"] == 0).all() and (got["lse"] == 0).all()
+    say("case fused one kept row")
+    m = np.zeros(200, np.uint8)
+    m[137] = 1
+    got = run_gpu_fused(x, mask=m, grad_loss=3.0)
+    check_full(x, got, oracle_full(x, grad_loss=3.0, mask=m), TOL["bf16"], 2e-3)
+
+
+def test_fused_large_logit_range():
+    # logits spread over ~+-60: exp(z - m) spans the whole fp32 exponent range
+    # within a row, where a fixed reference point would overflow or flush
+    x = _custom(300, 64, 3000, 17, "f32", seed=9)
+    x.W *= 40.0
+    say("case fused wide logit range fp32")
+    got = run_gpu_fused(x, chunk=1)
+    check_full(x, got, oracle_full(x), dict(loss_rel=1e-5, grad_rel=1e-4), 1e-4)
+
+
+def test_fused_output_dtypes_and_default_grad():
+    import torch
+    x = _custom(300, 96, 1500, 11)
+    say("case fused bf16 dH and dW outputs, grad_loss NULL")
+    got = run_gpu_fused(x, dh_dtype=torch.bfloat16, dw_dtype=torch.bfloat16, chunk=5, grad_loss=None)
+    check_full(x, got, oracle_full(x), TOL["bf16"], 2e-3)
+
+
+def test_fused_validate_reports_bad_indices():
+    import chunked_kl_loss_amd as ckl
+    x = _custom(50, 16, 200, 6)
+    run_gpu_fused(x, validate=True)
+    y = _custom(50, 16, 200, 6)
+    y.idx[9, 4] = y.idx[9, 1]
+    say("case fused validate repeat")
+    with pytest.raises(ckl.CklError) as e:
+        run_gpu_fused(y, validate=True)
+    assert e.value.status == 4
+    # unchecked, out-of-range and negative entries must not fault (they match
+    # no column); the call completes
+    y.idx[7, 2] = 200
+    y.idx[3, 0] = -1
+    say("case fused unchecked bad indices")
+    run_gpu_fused(y, validate=False)
+
+
+def test_fused_matches_two_call_path():
+    # the same loss up to the order of the split merges; gradients up to the
+    # extra bf16 rounding of exp(z - m)
+    x = inputs(1, T=1500)
+    say("case fused vs two-call")
+    a = run_gpu_fused(x, chunk=700, grad_loss=0.5)
+    b = run_gpu(x, chunk=700, grad_loss=0.5)
+    assert abs(a["loss"] - b["loss"]) <= 1e-6 * abs(b["loss"])
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=0, atol=1e-5)
+    np.testing.assert_allclose(a["row_loss"], b["row_loss"], rtol=1e-5, atol=1e-5)
+    assert max_rel(a["dH"], b["dH"]) <= 4e-3
+    assert max_rel(a["dW"], b["dW"]) <= 4e-3
+
+
+def test_fused_bitwise_deterministic():
+    x = inputs(1, T=1500)
+    say("case fused determinism")
+    a = run_gpu_fused(x, chunk=100)
+    b = run_gpu_fused(x, chunk=100)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "row_loss", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_fused_autograd_function():
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    from tests.gpu_harness import to_device
+    x = inputs(1, T=512)
+    H, W, idx, tl, m = to_device(x)
+    H.requires_grad_(True)
+    W.requires_grad_(True)
+    loss = ckl.chunked_kl_loss(H, W, idx, tl, m, chunk=256, fused=True)
+    (2.0 * loss).backward()
+    ref = oracle.kl_dense(x.H, x.W, x.idx, x.tlogit, grad_loss=2.0)
+    assert abs(loss.item() - ref["loss"]) <= 2e-3 * ref["loss"]
+    assert H.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
+    assert max_rel(H.grad.double().cpu().numpy(), ref["dH"]) <= 1e-2
+    assert max_rel(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-2
