@@ -209,9 +209,11 @@ def main():
     try:
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
-        ent = tr.get("kernels", {}).get(dom)
-        if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
-            traffic = ent["hbm_bytes_per_launch"]
+        for e in tr.get("entries", []):
+            ent = e.get("kernels", {}).get(dom)
+            if (ent and e.get("source_hash") == kernel_source_hash() and e.get("workload") == w.name
+                    and e.get("path") == args.path and chunk == w.chunk):
+                traffic = ent["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

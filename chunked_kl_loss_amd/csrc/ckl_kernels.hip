@@ -547,45 +547,59 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
   // all E entries of a chunk share the tile and the wave row block; entries
   // with bit 2 of v clear / set belong to lane groups h = 0 / 1
   const int64_t grp = ((int64_t)(vc / tile_m) * (tile_m / wave_rows) + (vc % tile_m) / wave_rows) * 2;
-  for (int i = rr; i < 128; i += RPP) {
-    const int t = t0 + i;
-    float f0 = 0.f, f1 = 0.f;
-    bool ok = false;
+  constexpr int NR = 128 / RPP;  // rows per thread
+  // all loads first (the in-place stores would otherwise order each row's
+  // load after the previous row's store, leaving one load in flight)
+  using VT = typename std::conditional<kBF16, u32x4, f32x4>::type;
+  VT x[NR];
+  float f0[NR], f1[NR];
+  bool ok[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int t = t0 + rr + j * RPP;
+    x[j] = *reinterpret_cast<const VT*>(G + (int64_t)t * ldG + vc);
+    f0[j] = 0.f;
+    f1[j] = 0.f;
+    ok[j] = false;
     if (t < rows) {
       const float sc = srow[t];
       if (sc != 0.f) {
-        ok = true;
+        ok[j] = true;
         const float coef = sc * Mrow[t];
         const float l2 = lse[t] * kLog2e;
-        f0 = coef * fast_exp2(mtab[grp * ldm + t] - l2);
-        f1 = coef * fast_exp2(mtab[(grp + 1) * ldm + t] - l2);
+        f0[j] = coef * fast_exp2(mtab[grp * ldm + t] - l2);
+        f1[j] = coef * fast_exp2(mtab[(grp + 1) * ldm + t] - l2);
       }
     }
-    TIn* gp = G + (int64_t)t * ldG + vc;
-    float g[E];
-    if constexpr (kBF16) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(gp);
+  }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float u = bf16_bits_to_f32((x[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        g[e] = (ok && vc + e < V) ? u * (((vc + e) & 4) ? f1 : f0) : 0.f;
-      }
+  for (int j = 0; j < NR; ++j) {
+    const int i = rr + j * RPP;
+    const int t = t0 + i;
+    // rows past `rows` and masked rows may hold stale u: select, never
+    // multiply, so that they come out as exact zeros
+    TIn* gp = G + (int64_t)t * ldG + vc;
+    if constexpr (kBF16) {
       u32x4 y;
 #pragma unroll
-      for (int e = 0; e < E; e += 2) y[e >> 1] = pack_bf16x2(g[e], g[e + 1]);
+      for (int e = 0; e < E; e += 2) {
+        const float u0 = bf16_bits_to_f32(x[j][e >> 1] & 0xffffu);
+        const float u1 = bf16_bits_to_f32(x[j][e >> 1] >> 16);
+        const float fe = (e & 4) ? f1[j] : f0[j];
+        const float g0 = (ok[j] && vc + e < V) ? u0 * fe : 0.f;
+        const float g1 = (ok[j] && vc + e + 1 < V) ? u1 * fe : 0.f;
+        y[e >> 1] = pack_bf16x2(g0, g1);
+      }
       *reinterpret_cast<u32x4*>(gp) = y;
 #pragma unroll
       for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = (uint16_t)((y[e >> 1] >> (16 * (e & 1))) & 0xffffu);
     } else {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(gp);
-#pragma unroll
-      for (int e = 0; e < E; ++e) g[e] = (ok && vc + e < V) ? x[e] * (((vc + e) & 4) ? f1 : f0) : 0.f;
       f32x4 y;
 #pragma unroll
-      for (int e = 0; e < E; ++e) y[e] = g[e];
+      for (int e = 0; e < E; ++e) y[e] = (ok[j] && vc + e < V) ? x[j][e] * (((vc + e) & 4) ? f1[j] : f0[j]) : 0.f;
       *reinterpret_cast<f32x4*>(gp) = y;
 #pragma unroll
-      for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = g[e];
+      for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = y[e];
     }
   }
   __syncthreads();

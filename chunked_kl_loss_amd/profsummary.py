@@ -2,13 +2,14 @@
 
     python -m chunked_kl_loss_amd.profsummary trace <kernel_stats.csv> <out.md> "<command>"
     python -m chunked_kl_loss_amd.profsummary traffic <fetch_counter.csv> <write_counter.csv> \\
-        <out.json> <workload> <steps>
+        <traffic.json> <workload> <path> <steps>
 
 `trace` condenses a --kernel-trace --stats run into a markdown table grouped by
 kernel class.  `traffic` takes the FETCH_SIZE and WRITE_SIZE passes (KiB per
 dispatch), scales them by what the same counters read for the plain 1 GiB
-copy that bench.py --copy-calibration runs, and writes HBM bytes per launch
-for every kernel class, tagged with the hash of the kernel sources.
+copy that bench.py --copy-calibration runs, and records HBM bytes per launch
+for every kernel class in traffic.json under (workload, path), tagged with the
+hash of the kernel sources (other entries of the file are kept).
 """
 from __future__ import annotations
 
@@ -18,8 +19,8 @@ import json
 import sys
 
 CLASSES = (("fwd_lse", "fwd_lse"), ("bwd_grad", "bwd_grad"), ("gemm_store", "gemm_dhdw"),
-           ("transpose_pad", "transpose"), ("teacher_prep", "teacher_prep"),
-           ("fwd_finalize", "fwd_finalize"))
+           ("gpass", "g_pass"), ("transpose_pad", "transpose"), ("teacher_prep", "teacher_prep"),
+           ("fwd_finalize", "fwd_finalize"), ("loss_reduce", "fwd_finalize"))
 
 
 def kernel_class(name: str) -> str:
@@ -63,7 +64,7 @@ def _per_dispatch(csv_path: str, counter: str):
     return out
 
 
-def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, steps: int) -> None:
+def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, path: str, steps: int) -> None:
     sys.path.insert(0, ".")
     from bench import kernel_source_hash
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
@@ -87,15 +88,20 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, steps:
             d["launches"] = len(v)
     for c, d in res.items():
         d["hbm_bytes_per_launch"] = d.get("hbm_read_bytes_per_launch", 0.0) + d.get("hbm_write_bytes_per_launch", 0.0)
-    json.dump({"workload": workload, "source_hash": kernel_source_hash(), "steps_profiled": steps,
-               "copy_scale": {"FETCH_SIZE": 1.0 / fscale, "WRITE_SIZE": 1.0 / wscale},
-               "kernels": res}, open(out_json, "w"), indent=1)
+    try:
+        doc = json.load(open(out_json))
+    except (OSError, ValueError):
+        doc = {}
+    entries = [e for e in doc.get("entries", []) if (e.get("workload"), e.get("path")) != (workload, path)]
+    entries.append({"workload": workload, "path": path, "source_hash": kernel_source_hash(), "steps_profiled": steps,
+                    "copy_scale": {"FETCH_SIZE": 1.0 / fscale, "WRITE_SIZE": 1.0 / wscale}, "kernels": res})
+    json.dump({"entries": entries}, open(out_json, "w"), indent=1)
 
 
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
-        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]))
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], int(sys.argv[7]))
     else:
         raise SystemExit(__doc__)
