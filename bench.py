@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--path", choices=("fused", "recompute"), default="fused",
                     help="one ckl_forward_backward call per step, or ckl_forward + ckl_backward")
+    ap.add_argument("--compare", action=argparse.BooleanOptionalAction, default=True,
+                    help="after the timed path, also time the other one (reported under other_path)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -137,65 +139,81 @@ def main():
     T, d, V, K = x.T, x.d, x.V, x.K
     in_code = B.CKL_BF16 if x.dtype == "bf16" else B.CKL_F32
     prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32)
-    fused = args.path == "fused"
-    plan = B.fused_plan(prob) if fused else B.backward_plan(prob)
-    ws_f = torch.empty(B.workspace_size(prob, 2 if fused else 0), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(1 if fused else B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(T, dtype=torch.float32, device=dev)
-    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
-    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     P = ctypes.byref(prob)
     mp = None if mask is None else mask.data_ptr()
+    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
 
-    def fwd():
-        B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, loss.data_ptr(),
-                                lse.data_ptr(), None, ws_f.data_ptr(), ws_f.numel(), sp), lib)
+    def measure(path: str, steps: int, warmup: int) -> dict:
+        """Time `steps` steps of one path (inputs already resident); per-kernel event timing included."""
+        fused = path == "fused"
+        plan = B.fused_plan(prob) if fused else B.backward_plan(prob)
+        torch.cuda.reset_peak_memory_stats(dev)
+        ws_f = torch.empty(B.workspace_size(prob, 2 if fused else 0), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(1 if fused else B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+        dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
 
-    def bwd():
-        B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, lse.data_ptr(),
-                                 None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(), ws_b.numel(), sp), lib)
+        def fwd():
+            B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                    loss.data_ptr(), lse.data_ptr(), None, ws_f.data_ptr(), ws_f.numel(), sp), lib)
 
-    def both():
-        B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp, None,
-                                         loss.data_ptr(), lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(),
-                                         ws_f.data_ptr(), ws_f.numel(), sp), lib)
+        def bwd():
+            B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                     lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(),
+                                     ws_b.numel(), sp), lib)
 
-    if fused:
-        fwd, bwd = both, (lambda: None)
-    log(f"warmup {args.warmup} steps; path {args.path}, plan {plan}")
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize(dev)
-    if not np.isfinite(loss.item()):
-        raise RuntimeError("non-finite loss")
+        def both():
+            B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                             None, loss.data_ptr(), lse.data_ptr(), None, dH.data_ptr(),
+                                             dW.data_ptr(), ws_f.data_ptr(), ws_f.numel(), sp), lib)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    ckl.timing_enable(True)
-    torch.cuda.synchronize(dev)
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
-        bwd()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t_start
-    ckl.timing_enable(False)
-    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = wall * 1e3 / args.steps
-    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
-    log(f"timed {args.steps} steps: {step_ms:.2f} ms/step (fwd {np.mean(fwd_ms):.2f}, bwd {np.mean(bwd_ms):.2f})")
+        if fused:
+            fwd, bwd = both, (lambda: None)
+        log(f"warmup {warmup} steps; path {path}, plan {plan}")
+        for _ in range(warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize(dev)
+        if not np.isfinite(loss.item()):
+            raise RuntimeError("non-finite loss")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        ckl.timing_enable(True)
+        torch.cuda.synchronize(dev)
+        t_start = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fwd()
+            ev[i][1].record(stream)
+            bwd()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t_start
+        ckl.timing_enable(False)
+        fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+        bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+        step_ms = wall * 1e3 / steps
+        peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+        log(f"timed {steps} steps, path {path}: {step_ms:.2f} ms/step")
+        kt = ckl.timing_read()
+        del ws_f, ws_b, dH, dW, loss, lse
+        torch.cuda.empty_cache()
+        return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, kt=kt,
+                    fwd_ms=None if fused else float(np.mean(fwd_ms)),
+                    bwd_ms=None if fused else float(np.mean(bwd_ms)),
+                    events_min_ms=float(np.min(np.add(fwd_ms, bwd_ms))))
+
+    m = measure(args.path, args.steps, args.warmup)
+    fused = args.path == "fused"
+    step_ms, kt, plan = m["step_ms"], m["kt"], m["plan"]
 
     # ---- per-kernel timing and roofline of the dominant kernel
-    kt = ckl.timing_read()
     flops_step = 8.0 * T * V * d
+    performed_step = (6.0 if fused else 8.0) * T * V * d
     algo_flops = {"fwd_lse": 2.0 * T * V * d, "gemm_dhdw": 4.0 * T * V * d}
     if not fused:
         algo_flops["bwd_grad"] = 2.0 * T * V * d
@@ -204,7 +222,6 @@ def main():
     dom = max(algo_flops, key=lambda k: kt[k][0])
     dom_ms, dom_n = kt[dom]
     achieved = algo_flops[dom] * args.steps / (dom_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     traffic = None
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -219,8 +236,8 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": traffic,
                 "avg_launch_ms": dom_ms / dom_n, "launches_per_step": dom_n / args.steps,
-                "algorithmic_flops_per_step": algo_flops[dom]}
-
+                "algorithmic_flops_per_step": algo_flops[dom],
+                "algorithmic_flops_per_launch": algo_flops[dom] / (dom_n / args.steps)}
     tokens_s = T / (step_ms * 1e-3)
     tflops = flops_step / (step_ms * 1e-3) / 1e12
     n_valid = int(T if x.mask is None else x.mask.sum())
@@ -242,18 +259,26 @@ def main():
                    "masked_rows": T - n_valid, "parallelism": "single GPU", "path": args.path,
                    "plan": plan},
         "tflops": tflops,
-        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        "tflops_note": "8 T V d useful flops per step (forward, recomputed logits, dH, dW); the fused path "
-                       "multiplies 6 T V d of them" if fused else "8 T V d flops per step, all multiplied",
-        "peak_hbm_gib": peak_gib,
-        "fwd_ms": None if fused else float(np.mean(fwd_ms)),
-        "bwd_ms": None if fused else float(np.mean(bwd_ms)),
-        "step_ms_events_min": float(np.min(np.add(fwd_ms, bwd_ms))),
+        "tflops_note": "8 T V d flops per step, the method's count (forward, recomputed logits, dH, dW)"
+                       + ("; the fused path multiplies 6 T V d of them (no recompute)" if fused else ""),
+        "tflops_multiplied": performed_step / (step_ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * performed_step / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "peak_hbm_gib": m["peak_gib"],
+        "fwd_ms": m["fwd_ms"],
+        "bwd_ms": m["bwd_ms"],
+        "step_ms_events_min": m["events_min_ms"],
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    del H, W, idx, tl, mask, ws_f, ws_b, dH, dW
+    if args.compare:
+        other = "recompute" if fused else "fused"
+        o = measure(other, args.steps, args.warmup)
+        result["other_path"] = {"path": other, "ms_per_step": o["step_ms"], "tokens_per_s": T / (o["step_ms"] * 1e-3),
+                                "peak_hbm_gib": o["peak_gib"], "fwd_ms": o["fwd_ms"], "bwd_ms": o["bwd_ms"],
+                                "plan": o["plan"],
+                                "kernels_ms_per_step": {k: ms / args.steps for k, (ms, n) in o["kt"].items() if n}}
+    del H, W, idx, tl, mask
     torch.cuda.empty_cache()
     if args.copy_calibration:
         # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB

@@ -15,7 +15,9 @@ At these sizes the fp64 oracle cannot evaluate everything, so the checks are:
     equal to c the student distribution is uniform, so LSE_t = h_t . c + ln V
     and dW[v] = sum_t s_t (1/V - p_t[v]) h_t.
 Tolerances as in the element-wise tests (bf16 inputs: loss 2e-3 relative,
-dH / dW 1e-2 of the largest reference magnitude).
+dH / dW 1e-2 of the largest reference magnitude).  The one-call path
+(ckl_forward_backward) gets the same sampled-row and property checks at the
+benchmark workload and on the packed-document workload.
 """
 import math
 
@@ -24,7 +26,7 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, make_inputs
-from tests.gpu_harness import TOL, run_gpu, say
+from tests.gpu_harness import TOL, run_gpu, run_gpu_fused, say
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +180,53 @@ def test_full_size_equal_rows_closed_form():
     # dH is (sum_v G[t, v]) c: zero up to the bf16 rounding of G
     g_abs = s * 2.0  # sum_v |G[t, v]| <= s (M + sum p) = 2 s
     assert np.abs(got["dH"]).max() <= 1e-2 * g_abs * np.abs(c).max()
+
+
+def sample_rows_fused(x, chunk, n_random=24, seed=1):
+    import chunked_kl_loss_amd as ckl
+    plan = ckl.fused_plan(ckl.make_problem(x.T, x.d, x.V, x.K, chunk))
+    T = x.T
+    rows = {0, 1, 255, 256, T - 1, T - 2}
+    for c in range(1, plan["chunks"]):
+        rows.update({c * plan["rows"] - 1, c * plan["rows"]})
+    if x.mask is not None:
+        starts = np.nonzero(np.diff(x.mask.astype(np.int8)) == 1)[0] + 1
+        rows.update(int(s) for s in starts[:8])
+        rows.update(int(s) - 1 for s in starts[:8])
+    rng = np.random.default_rng(seed)
+    rows.update(int(r) for r in rng.integers(0, T, n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < T)), plan
+
+
+def test_fused_full_size_headline():
+    x = inputs(2)
+    rows, plan = sample_rows_fused(x, x.chunk)
+    say(f"case fused cfg2 full T={x.T} chunk={x.chunk} plan={plan} rows={rows.size}")
+    got = run_gpu_fused(x)
+    e = check_rows(x, got, rows)
+    check_properties(x, got)
+    say(f"  sampled dH rel err {e:.2e}, loss {got['loss']:.6f}")
+    # agreement with the recomputing two-call path over the whole problem
+    ref = run_gpu(x)
+    assert abs(got["loss"] - ref["loss"]) <= 1e-6 * abs(ref["loss"])
+    np.testing.assert_allclose(got["lse"], ref["lse"], rtol=0, atol=1e-5)
+    # dW is fp32 out: the paths differ by G's extra rounding only (u rounded
+    # to bf16 before rescaling, <= 2^-9 relative per entry).  dH is bf16 out:
+    # add one bf16 ulp of the largest entry (2^-8 of max|dH|) for two sums
+    # that round to neighbouring bf16 values.
+    bound = {"dW": 4e-3, "dH": 2.0 ** -8 + 2 * 2.0 ** -9}
+    for k in ("dH", "dW"):
+        err = np.abs(got[k] - ref[k]).max() / np.abs(ref[k]).max()
+        say(f"  fused vs two-call {k}: {err:.2e}")
+        assert err <= bound[k], (k, err)
+
+
+@pytest.mark.parametrize("chunk", [512, 8192])
+def test_fused_packed_documents(chunk):
+    x = inputs(4)
+    rows, plan = sample_rows_fused(x, chunk, n_random=16)
+    say(f"case fused cfg4 full T={x.T} chunk={chunk} plan={plan}")
+    got = run_gpu_fused(x, chunk=chunk)
+    check_rows(x, got, rows)
+    check_properties(x, got)
+    del got

@@ -141,7 +141,9 @@ def test_fused_matches_two_call_path():
     assert abs(a["loss"] - b["loss"]) <= 1e-6 * abs(b["loss"])
     np.testing.assert_allclose(a["lse"], b["lse"], rtol=0, atol=1e-5)
     np.testing.assert_allclose(a["row_loss"], b["row_loss"], rtol=1e-5, atol=1e-5)
-    assert max_rel(a["dH"], b["dH"]) <= 4e-3
+    # dW fp32 out: G's extra rounding only; dH bf16 out: plus one bf16 ulp of
+    # the largest entry (see the full-size test)
+    assert max_rel(a["dH"], b["dH"]) <= 2.0 ** -8 + 2 * 2.0 ** -9
     assert max_rel(a["dW"], b["dW"]) <= 4e-3
 
 
