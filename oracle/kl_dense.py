@@ -30,6 +30,15 @@ What is computed is the Full Dense KL baseline of [README], step by step:
      G[t, v] = s_t * (M_t q[t, v] - P[t, v]), where M_t = sum_v P[t, v]
      (the teacher mass of the README formula); dH = G W and dW = G^T H.
 
+Teacher forms.  ``teacher_form = 0`` (the default): the cached entries are
+logits, renormalised over the K entries (M = 1 up to rounding).
+``teacher_form = 1``: the cached entries are the teacher's log-probabilities
+over its full vocabulary, truncated to the top K and used as given, so
+p = exp(entry) and the mass M = sum_k p_k may be below 1 -- the general case
+the README formula carries M for.  Steps 2-6 are unchanged: the per-row value
+is sum_v p log p - sum_v p log q over the support, which is the README sparse
+form with that M.
+
 Readings where the pages are silent or garbled (the formula's definition of M
 and the closed-form gradient were lost from the README text):
   * M is the teacher mass on its support, forced by expanding KL(p || q)
@@ -52,13 +61,20 @@ import numpy as np
 _F64 = np.float64
 
 
-def teacher_probs(tlogit: np.ndarray) -> np.ndarray:
-    """Step 1: p[t, k] = softmax over k of the cached teacher logits (fp64).
+def teacher_probs(tlogit: np.ndarray, teacher_form: int = 0) -> np.ndarray:
+    """Step 1: the teacher probabilities p[t, k] (fp64).
 
-    Follows [POST] (top-100 logits are cached) and [README] (the loss is
-    evaluated against cached top-K teacher probabilities).
+    teacher_form 0: softmax over k of the cached teacher logits, following
+    [POST] (top-100 logits are cached) and [README] (the loss is evaluated
+    against cached top-K teacher probabilities).  teacher_form 1: the cached
+    entries are log-probabilities; p = exp(entry), not renormalised (the
+    teacher mass M of the [README] formula is then sum_k p_k).
     """
     a = np.asarray(tlogit, dtype=_F64)
+    if teacher_form == 1:
+        return np.exp(a)
+    if teacher_form != 0:
+        raise ValueError("teacher_form must be 0 (logits) or 1 (log-probabilities)")
     a = a - a.max(axis=1, keepdims=True)
     e = np.exp(a)
     return e / e.sum(axis=1, keepdims=True)
@@ -111,7 +127,7 @@ def _block(H64, W64, idx_b, p_b, s_b, V, want_grads):
 
 
 def kl_dense(H, W, idx, tlogit, mask=None, grad_loss: float = 1.0, block: int = 256,
-             want_grads: bool = True):
+             want_grads: bool = True, teacher_form: int = 0):
     """Full Dense KL loss, per-row LSE / KL, dH and dW in fp64.
 
     Returns a dict with ``loss`` (float), ``lse`` [T], ``row_loss`` [T] (both
@@ -123,7 +139,7 @@ def kl_dense(H, W, idx, tlogit, mask=None, grad_loss: float = 1.0, block: int = 
     T, d = H.shape
     V = W.shape[0]
     W64 = W.astype(_F64)
-    p = teacher_probs(tlogit)
+    p = teacher_probs(tlogit, teacher_form)
     keep, N, s = row_scale(mask, T, grad_loss)
     lse = np.empty(T, dtype=_F64)
     row_loss = np.empty(T, dtype=_F64)
@@ -142,7 +158,8 @@ def kl_dense(H, W, idx, tlogit, mask=None, grad_loss: float = 1.0, block: int = 
     return dict(loss=loss, lse=lse, row_loss=row_loss, dH=dH, dW=dW, N=N, keep=keep)
 
 
-def kl_rows(H, W, idx, tlogit, rows, mask=None, grad_loss: float = 1.0, block: int = 64):
+def kl_rows(H, W, idx, tlogit, rows, mask=None, grad_loss: float = 1.0, block: int = 64,
+            teacher_form: int = 0):
     """The same quantities for selected rows only: lse, row_loss and dH rows.
 
     Each row's values depend on that row alone (plus N through the mask), so
@@ -153,7 +170,7 @@ def kl_rows(H, W, idx, tlogit, rows, mask=None, grad_loss: float = 1.0, block: i
     V = np.asarray(W).shape[0]
     W64 = np.asarray(W).astype(_F64)
     _, N, s = row_scale(mask, T, grad_loss)
-    p = teacher_probs(np.asarray(tlogit)[rows])
+    p = teacher_probs(np.asarray(tlogit)[rows], teacher_form)
     out_lse = np.empty(rows.size, dtype=_F64)
     out_loss = np.empty(rows.size, dtype=_F64)
     out_dH = np.empty((rows.size, W64.shape[1]), dtype=_F64)
@@ -178,7 +195,7 @@ def lse_rows(H, W, block: int = 256) -> np.ndarray:
 
 
 def dw_rows(H, W, idx, tlogit, vrows, lse, mask=None, grad_loss: float = 1.0,
-            block: int = 4096) -> np.ndarray:
+            block: int = 4096, teacher_form: int = 0) -> np.ndarray:
     """Rows ``vrows`` of dW = G^T H, given the fp64 LSE of every row (from
     ``lse_rows``).  Column v of G only needs z[:, v] = H w_v and the teacher
     entries equal to v."""
@@ -186,7 +203,7 @@ def dw_rows(H, W, idx, tlogit, vrows, lse, mask=None, grad_loss: float = 1.0,
     T = H.shape[0]
     vrows = np.asarray(vrows, dtype=np.int64)
     Wsel = np.asarray(W)[vrows].astype(_F64)          # [R, d]
-    p = teacher_probs(tlogit)
+    p = teacher_probs(tlogit, teacher_form)
     _, N, s = row_scale(mask, T, grad_loss)
     M = p.sum(axis=1)
     # teacher probability at (t, vrows[j]); zero when vrows[j] is not in S_t
@@ -206,7 +223,7 @@ def dw_rows(H, W, idx, tlogit, vrows, lse, mask=None, grad_loss: float = 1.0,
     return out
 
 
-def kl_sparse_loss(H, W, idx, tlogit, mask=None, block: int = 256):
+def kl_sparse_loss(H, W, idx, tlogit, mask=None, block: int = 256, teacher_form: int = 0):
     """The README's sparse form of the same objective, evaluated separately:
     l_t = sum_k p log p - sum_k p z[t, idx_k] + M_t * logsumexp(z_t),
     with only the log-normaliser spanning the vocabulary.  Returns
@@ -214,7 +231,7 @@ def kl_sparse_loss(H, W, idx, tlogit, mask=None, block: int = 256):
     H = np.asarray(H)
     W64 = np.asarray(W).astype(_F64)
     T = H.shape[0]
-    p = teacher_probs(tlogit)
+    p = teacher_probs(tlogit, teacher_form)
     keep, N, _ = row_scale(mask, T)
     row_loss = np.empty(T, dtype=_F64)
     idx = np.asarray(idx, dtype=np.int64)

@@ -43,7 +43,8 @@ def test_hand_worked_examples(case):
     idx = np.array(case["idx"], dtype=np.int32)
     tl = np.array(case["tlogit"], dtype=np.float64)
     mask = None if case["mask"] is None else np.array(case["mask"], dtype=np.uint8)
-    r = oracle.kl_dense(H, W, idx, tl, mask=mask, grad_loss=case["grad_loss"], block=1)
+    r = oracle.kl_dense(H, W, idx, tl, mask=mask, grad_loss=case["grad_loss"], block=1,
+                        teacher_form=case.get("teacher_form", 0))
     assert r["loss"] == pytest.approx(case["loss"], rel=1e-13, abs=1e-15)
     np.testing.assert_allclose(r["lse"], case["lse"], rtol=1e-13)
     for got, want in zip(r["row_loss"], case["row_loss"]):
@@ -315,3 +316,81 @@ def test_generator_recipe():
         assert 512 <= L <= 8192
         n0 = int(round(0.25 * L))
         assert (m[a:a + n0] == 0).all() and (m[a + n0:b] == 1).all()
+
+
+# ------------------------------------- teacher form 1: log-probabilities ----
+def _truncated_logprobs(rng, T, K, extra=50):
+    """Top-K log-probabilities of a softmax over K + extra classes: mass < 1."""
+    full = rng.normal(0.0, 2.0, size=(T, K + extra))
+    full -= full.max(axis=1, keepdims=True)
+    logp = full - np.log(np.exp(full).sum(axis=1, keepdims=True))
+    return np.sort(logp, axis=1)[:, ::-1][:, :K].copy()
+
+
+def test_logprob_form_reduces_to_logits_when_normalised():
+    # log-probabilities that sum to one (scipy's log_softmax of the logits)
+    # describe the same teacher as the logits themselves
+    special = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(21)
+    H, W, idx, tl, mask = _rand_problem(rng, 20, 12, 90, 7, scale=1.5, masked=True)
+    a = oracle.kl_dense(H, W, idx, tl, mask=mask, grad_loss=0.7)
+    b = oracle.kl_dense(H, W, idx, special.log_softmax(tl, axis=1), mask=mask, grad_loss=0.7, teacher_form=1)
+    assert b["loss"] == pytest.approx(a["loss"], rel=1e-12)
+    np.testing.assert_allclose(b["row_loss"], a["row_loss"], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(b["dH"], a["dH"], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(b["dW"], a["dW"], rtol=1e-10, atol=1e-15)
+
+
+@pytest.mark.parametrize("alpha", [0.25, 0.9])
+def test_truncated_mass_scaling_closed_form(alpha):
+    # p = alpha * softmax(l): the row value is alpha * (l_1 + log alpha) where
+    # l_1 is the value for the normalised teacher (the M * LSE term carries
+    # alpha), and the logit gradient s (M q - p) scales by alpha
+    rng = np.random.default_rng(22)
+    H, W, idx, tl, mask = _rand_problem(rng, 16, 10, 70, 6, scale=1.2, masked=True)
+    one = oracle.kl_dense(H, W, idx, tl, mask=mask, grad_loss=1.3)
+    lp = np.log(alpha) + (tl - tl.max(axis=1, keepdims=True))
+    lp -= np.log(np.exp(tl - tl.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True))
+    r = oracle.kl_dense(H, W, idx, lp, mask=mask, grad_loss=1.3, teacher_form=1)
+    np.testing.assert_allclose(r["row_loss"], alpha * (one["row_loss"] + math.log(alpha)), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["dH"], alpha * one["dH"], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(r["dW"], alpha * one["dW"], rtol=1e-10, atol=1e-15)
+
+
+def test_logprob_form_gradients_match_central_differences():
+    rng = np.random.default_rng(23)
+    T, d, V, K = 4, 6, 14, 4
+    H, W, idx, _, mask = _rand_problem(rng, T, d, V, K, masked=True)
+    lp = _truncated_logprobs(rng, T, K)
+    assert (np.exp(lp).sum(axis=1) < 0.999).all()   # a real mass deficit
+    g = 0.9
+    r = oracle.kl_dense(H, W, idx, lp, mask=mask, grad_loss=g, teacher_form=1)
+    h = 1e-6
+
+    def f(Hx, Wx):
+        return g * oracle.kl_dense(Hx, Wx, idx, lp, mask=mask, want_grads=False, teacher_form=1)["loss"]
+
+    num_dH = np.zeros_like(H)
+    for i in range(T):
+        for j in range(d):
+            Hp = H.copy(); Hp[i, j] += h
+            Hm = H.copy(); Hm[i, j] -= h
+            num_dH[i, j] = (f(Hp, W) - f(Hm, W)) / (2 * h)
+    num_dW = np.zeros_like(W)
+    for i in range(V):
+        for j in range(d):
+            Wp = W.copy(); Wp[i, j] += h
+            Wm = W.copy(); Wm[i, j] -= h
+            num_dW[i, j] = (f(H, Wp) - f(H, Wm)) / (2 * h)
+    assert np.abs(r["dH"] - num_dH).max() <= 1e-7 * np.abs(num_dH).max() + 1e-12
+    assert np.abs(r["dW"] - num_dW).max() <= 1e-7 * np.abs(num_dW).max() + 1e-12
+
+
+def test_logprob_form_sparse_equals_dense():
+    rng = np.random.default_rng(24)
+    H, W, idx, _, mask = _rand_problem(rng, 30, 16, 200, 10, scale=2.0, masked=True)
+    lp = _truncated_logprobs(rng, 30, 10)
+    dense = oracle.kl_dense(H, W, idx, lp, mask=mask, want_grads=False, teacher_form=1)
+    loss, rows = oracle.kl_sparse_loss(H, W, idx, lp, mask=mask, teacher_form=1)
+    assert loss == pytest.approx(dense["loss"], rel=1e-12)
+    np.testing.assert_allclose(rows, dense["row_loss"], rtol=1e-11, atol=1e-13)
