@@ -243,6 +243,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes from `base`: loads at
+// offsets past `bytes` return zeros.  Word 3 is the gfx9-family default for
+// raw dword access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// An offset past any record the library builds (buffers stay below 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// buffer_load_dwordx4 ... lds: 16 bytes per lane at voffset + soffset into LDS
+// at `lds` + 16 * lane.
+__device__ __forceinline__ void lds_dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+}
+
 // vmcnt(n) for n < 64 (expcnt and lgkmcnt left unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -719,11 +733,16 @@ __device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __re
 // whose epilogue state leaves no room for it): each stage is then read and
 // multiplied one k16 substep at a time, and the finished stage is refilled
 // right after the barrier that starts the next one.
-template <int BM_, int BN_, int WM_, int WN_, int PIPE_ = 1>
+//
+// BUF = 0 issues global_load_lds with per-lane 64-bit addresses (rows past the
+// end re-read row 0, chunks past kdim read a zero block) instead of buffer
+// loads; it needs fewer scalar registers, which the recomputing backward's
+// epilogue wants.
+template <int BM_, int BN_, int WM_, int WN_, int PIPE_ = 1, int BUF_ = 1>
 struct Dma64Cfg {
   using TIn = bf16_t;
   using TileT = DmaTile<Dma64Cfg>;
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 2, PIPE = PIPE_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 2, PIPE = PIPE_, BUF = BUF_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NTHREADS = 64 * NWAVES;
@@ -742,8 +761,9 @@ struct Dma64Cfg {
 };
 
 // Same contract as tile_mma_dma (kdim a multiple of 8; k past kdim reads as
-// zero; rows past xrows / yrows give garbage outputs to discard; 32-bit row
-// offsets; ends with a barrier).
+// zero; rows past xrows / yrows give garbage outputs to discard; ends with a
+// barrier), except that offsets are in bytes: BM * ldx * 2 and BN * ldy * 2
+// must stay below 2^31.
 template <class C>
 __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
                                              const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
@@ -762,33 +782,53 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
 
-  // Loader: lane -> (row within its 8-row group, slot).  The rows of load i
-  // are (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for every
-  // i since NWAVES is even.
+  // Loader: buffer_load ... lds through one buffer resource per operand,
+  // based at the tile's first row and bounded by its valid rows, so rows past
+  // xrows / yrows read as zero without a clamp.  Lane -> (row within its 8-row
+  // group, slot); the rows of load i are (wave + i NWAVES) 8 + lrow, whose
+  // (r >> 1) & 7 is the same for every i since NWAVES is even.  The per-lane
+  // byte offsets stay fixed; the k slice advances in the scalar offset.
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
-  uint32_t off[C::LOADS_PER_STAGE];
-#pragma unroll
-  for (int i = 0; i < C::X_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 8 + lrow;
-    off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < C::Y_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 8 + lrow;
-    off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-  }
   auto lds_at = [&](int kt, int i) {
     char* st = smem + (kt & 1) * C::STAGE_BYTES;
     return i < C::X_LOADS ? st + (wave + i * C::NWAVES) * 1024
                           : st + C::X_BYTES + (wave + (i - C::X_LOADS) * C::NWAVES) * 1024;
   };
-  // load i of slice kt; `whole`: the slice lies inside [0, kdim)
+  uint32_t off[C::LOADS_PER_STAGE];
+  // (unused, and dropped by the compiler, when BUF = 0)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(min(xrows, C::BM) * ldx * 2));
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y, (uint32_t)(min(yrows, C::BN) * ldy * 2));
+  if constexpr (C::BUF) {
+#pragma unroll
+    for (int i = 0; i < C::X_LOADS; ++i)
+      off[i] = (uint32_t)(((wave + i * C::NWAVES) * 8 + lrow) * ldx * 2 + lchunk * 16);
+#pragma unroll
+    for (int i = 0; i < C::Y_LOADS; ++i)
+      off[C::X_LOADS + i] = (uint32_t)(((wave + i * C::NWAVES) * 8 + lrow) * ldy * 2 + lchunk * 16);
+  } else {  // element offsets; rows past the end re-read row 0
+#pragma unroll
+    for (int i = 0; i < C::X_LOADS; ++i) {
+      const int row = (wave + i * C::NWAVES) * 8 + lrow;
+      off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C::Y_LOADS; ++i) {
+      const int row = (wave + i * C::NWAVES) * 8 + lrow;
+      off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
+    }
+  }
+  // load i of slice kt; `whole`: the slice lies inside [0, kdim).  Chunks past
+  // kdim load zeros: an offset past every record (buffer loads) or the zero
+  // block.
   auto dma = [&](int kt, int i, bool whole) {
-    const int k0 = kt * C::BK;
-    const bf16_t* src = (i < C::X_LOADS ? X : Y) + k0 + off[i];
-    const void* g = (whole || k0 + lchunk * 8 < kdim) ? (const void*)src : (const void*)kZeroChunk;
-    lds_dma16(g, lds_at(kt, i));
+    const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
+    if constexpr (C::BUF) {
+      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? off[i] : kOutOfRange, (uint32_t)(kt * C::BK * 2), lds_at(kt, i));
+    } else {
+      const bf16_t* src = (i < C::X_LOADS ? X : Y) + kt * C::BK + off[i];
+      lds_dma16(in ? (const void*)src : (const void*)kZeroChunk, lds_at(kt, i));
+    }
   };
 
   // Reader: lane reads row (lane & 31) + 32 block of its wave's rows, chunk
