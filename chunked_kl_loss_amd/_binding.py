@@ -20,6 +20,8 @@ CKL_ERR_BAD_INDEX = 4
 CKL_ERR_HIP = 5
 CKL_F32 = 0
 CKL_BF16 = 1
+CKL_TEACHER_LOGITS = 0
+CKL_TEACHER_LOGPROBS = 1
 
 EXPORTED = (
     "ckl_workspace_size",
@@ -53,6 +55,7 @@ class Problem(ctypes.Structure):
         ("dh_dtype", ctypes.c_int32),
         ("dw_dtype", ctypes.c_int32),
         ("validate", ctypes.c_int32),
+        ("teacher_form", ctypes.c_int32),
     ]
 
 
@@ -104,9 +107,11 @@ def check(status: int, lib=None) -> None:
         raise CklError(status, lib.ckl_last_error().decode())
 
 
-def make_problem(T, d, V, K, chunk, in_dtype=CKL_BF16, dh_dtype=None, dw_dtype=CKL_F32, validate=False) -> Problem:
+def make_problem(T, d, V, K, chunk, in_dtype=CKL_BF16, dh_dtype=None, dw_dtype=CKL_F32, validate=False,
+                 teacher_form=CKL_TEACHER_LOGITS) -> Problem:
     return Problem(int(T), int(d), int(V), int(K), int(chunk), int(in_dtype),
-                   int(in_dtype if dh_dtype is None else dh_dtype), int(dw_dtype), int(bool(validate)))
+                   int(in_dtype if dh_dtype is None else dh_dtype), int(dw_dtype), int(bool(validate)),
+                   int(teacher_form))
 
 
 def workspace_size(prob: Problem, which: int) -> int:
@@ -200,13 +205,14 @@ def _stream_ptr(device):
 
 
 def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = False,
-            want_row_loss: bool = False):
-    """Returns (loss [1] float32, lse [T] float32, row_loss [T] or None)."""
+            want_row_loss: bool = False, teacher_form: int = CKL_TEACHER_LOGITS):
+    """Returns (loss [1] float32, lse [T] float32, row_loss [T] or None).  tlogit holds teacher logits
+    (teacher_form 0) or truncated teacher log-probabilities used as given (teacher_form 1)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
     T, d = H.shape
     V, K = W.shape[0], idx.shape[1]
-    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate)
+    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate, teacher_form=teacher_form)
     lib = load_library()
     ws_bytes = workspace_size(prob, 0)
     dev = H.device
@@ -221,7 +227,7 @@ def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = Fa
 
 
 def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh_dtype=None,
-             dw_dtype=None, validate: bool = False):
+             dw_dtype=None, validate: bool = False, teacher_form: int = CKL_TEACHER_LOGITS):
     """Returns (dH, dW) of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
@@ -230,7 +236,7 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     in_code = _dtype_code(H.dtype)
     dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
     dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
-    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form)
     lib = load_library()
     ws_bytes = workspace_size(prob, 1)
     dev = H.device
@@ -246,7 +252,8 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
 
 
 def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 2048, dh_dtype=None,
-                     dw_dtype=None, validate: bool = False, want_row_loss: bool = False):
+                     dw_dtype=None, validate: bool = False, want_row_loss: bool = False,
+                     teacher_form: int = CKL_TEACHER_LOGITS):
     """One call, no logit recompute: returns (loss [1], lse [T], row_loss [T] or None, dH, dW), the
     gradients being those of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
     torch = _torch()
@@ -256,7 +263,7 @@ def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 
     in_code = _dtype_code(H.dtype)
     dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
     dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
-    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form)
     lib = load_library()
     ws_bytes = workspace_size(prob, 2)
     dev = H.device

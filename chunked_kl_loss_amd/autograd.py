@@ -15,11 +15,12 @@ from . import _binding
 
 class ChunkedKLLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048):
-        loss, lse, _ = _binding.forward(H, W, idx, tlogit, mask, chunk=chunk)
+    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048, teacher_form: int = 0):
+        loss, lse, _ = _binding.forward(H, W, idx, tlogit, mask, chunk=chunk, teacher_form=teacher_form)
         ctx.save_for_backward(H, W, idx, tlogit, lse, mask if mask is not None else torch.empty(0))
         ctx.has_mask = mask is not None
         ctx.chunk = chunk
+        ctx.teacher_form = teacher_form
         return loss[0]
 
     @staticmethod
@@ -28,15 +29,16 @@ class ChunkedKLLoss(torch.autograd.Function):
         mask = mask if ctx.has_mask else None
         g = grad.reshape(1).to(torch.float32)
         dH, dW = _binding.backward(H, W, idx, tlogit, mask, lse, g, chunk=ctx.chunk,
-                                   dh_dtype=H.dtype, dw_dtype=W.dtype)
-        return dH, dW, None, None, None, None
+                                   dh_dtype=H.dtype, dw_dtype=W.dtype, teacher_form=ctx.teacher_form)
+        return dH, dW, None, None, None, None, None
 
 
 class FusedChunkedKLLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048):
+    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048, teacher_form: int = 0):
         loss, _, _, dH, dW = _binding.forward_backward(H, W, idx, tlogit, mask, None, chunk=chunk,
-                                                       dh_dtype=H.dtype, dw_dtype=W.dtype)
+                                                       dh_dtype=H.dtype, dw_dtype=W.dtype,
+                                                       teacher_form=teacher_form)
         ctx.save_for_backward(dH, dW)
         return loss[0]
 
@@ -44,13 +46,15 @@ class FusedChunkedKLLoss(torch.autograd.Function):
     def backward(ctx, grad):
         dH, dW = ctx.saved_tensors
         g = grad.to(torch.float32)
-        return ((dH.float() * g).to(dH.dtype), (dW.float() * g).to(dW.dtype), None, None, None, None)
+        return ((dH.float() * g).to(dH.dtype), (dW.float() * g).to(dW.dtype), None, None, None, None, None)
 
 
-def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False):
+def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False, teacher_form: int = 0):
     """Mean forward KL(teacher || student) over unmasked rows, differentiable
     with respect to H and W.  fused=True computes the gradients together with
-    the loss (one pass over the logits, chunk x V extra workspace)."""
+    the loss (one pass over the logits, chunk x V extra workspace).
+    teacher_form 1: tlogit holds truncated teacher log-probabilities, used as
+    given (teacher mass below one)."""
     if fused:
-        return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk)
-    return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk)
+        return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)
+    return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)

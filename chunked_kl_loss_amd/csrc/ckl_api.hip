@@ -39,7 +39,9 @@ ckl_status hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 constexpr int64_t kMaxK = 4096;
-constexpr int64_t kMaxRows = (int64_t)1 << 30;
+// Rows of H and W: the contraction loads address a 256-row tile of H^T, W^T,
+// G or G^T with 32-bit byte offsets (256 * (rows + padding) * 2 < 2^31).
+constexpr int64_t kMaxRows = 4000000;
 // Compute units of an MI355X; the logit and contraction kernels fit one
 // workgroup per CU (128 KiB of LDS each), so kCUs workgroups make one wave.
 constexpr int64_t kCUs = 256;
@@ -147,8 +149,11 @@ void pick_splits(int64_t row_blocks, int64_t vtiles, int64_t* splits, int64_t* t
 
 ckl_status check_problem(const ckl_problem* p) {
   if (!p) return fail(CKL_ERR_INVALID_ARG, "problem is NULL");
-  if (p->T < 1 || p->T > kMaxRows) return fail(CKL_ERR_INVALID_ARG, "T=%lld out of range [1, 2^30]", (long long)p->T);
-  if (p->V < 1 || p->V > kMaxRows) return fail(CKL_ERR_INVALID_ARG, "V=%lld out of range [1, 2^30]", (long long)p->V);
+  if (p->T < 1) return fail(CKL_ERR_INVALID_ARG, "T=%lld must be >= 1", (long long)p->T);
+  if (p->V < 1) return fail(CKL_ERR_INVALID_ARG, "V=%lld must be >= 1", (long long)p->V);
+  if (p->T > kMaxRows || p->V > kMaxRows)
+    return fail(CKL_ERR_UNSUPPORTED, "T=%lld, V=%lld: at most %lld rows each", (long long)p->T, (long long)p->V,
+                (long long)kMaxRows);
   if (p->d < 8 || p->d % 8 != 0) return fail(CKL_ERR_INVALID_ARG, "d=%lld must be a positive multiple of 8", (long long)p->d);
   if (p->d > 65536) return fail(CKL_ERR_UNSUPPORTED, "d=%lld exceeds 65536", (long long)p->d);
   if (p->K < 1 || p->K > p->V) return fail(CKL_ERR_INVALID_ARG, "K=%lld must satisfy 1 <= K <= V", (long long)p->K);
@@ -159,6 +164,8 @@ ckl_status check_problem(const ckl_problem* p) {
   if (!dt_ok(p->in_dtype) || !dt_ok(p->dh_dtype) || !dt_ok(p->dw_dtype))
     return fail(CKL_ERR_INVALID_ARG, "dtype codes must be CKL_F32 (0) or CKL_BF16 (1)");
   if (p->validate != 0 && p->validate != 1) return fail(CKL_ERR_INVALID_ARG, "validate must be 0 or 1");
+  if (p->teacher_form != CKL_TEACHER_LOGITS && p->teacher_form != CKL_TEACHER_LOGPROBS)
+    return fail(CKL_ERR_INVALID_ARG, "teacher_form must be CKL_TEACHER_LOGITS (0) or CKL_TEACHER_LOGPROBS (1)");
   return CKL_OK;
 }
 
@@ -338,7 +345,7 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
-                                                  p->validate ? bad : nullptr, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
   if (p->validate) {
@@ -400,7 +407,7 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, nullptr, M, nullptr,
-                                                  p->validate ? bad : nullptr, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
   if (p->validate) {
@@ -498,7 +505,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
-                                                  p->validate ? bad : nullptr, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
   if (p->validate) {
@@ -634,6 +641,6 @@ const char* ckl_status_string(ckl_status s) {
 
 const char* ckl_last_error(void) { return g_last_error.c_str(); }
 
-int32_t ckl_version(void) { return (1 << 16) | 0; }
+int32_t ckl_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
                                                           int T, int K, int Kp, int V, int* __restrict__ idx_s,
                                                           float* __restrict__ p_s, float* __restrict__ Erow,
                                                           float* __restrict__ Mrow, float* __restrict__ zg_s,
-                                                          int* __restrict__ bad) {
+                                                          int* __restrict__ bad, int logprob) {
   extern __shared__ int sm_dyn[];
   int* key = sm_dyn;
   float* val = reinterpret_cast<float*>(sm_dyn + Kp);
@@ -126,20 +126,25 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
   const int* irow = idx + (int64_t)t * K;
   const float* lrow = tlogit + (int64_t)t * K;
 
-  float mx = -INFINITY;
-  for (int k = lane; k < K; k += 64) mx = fmaxf(mx, lrow[k]);
-  mx = wave_max(mx);
-  float se = 0.f;
-  for (int k = lane; k < K; k += 64) se += expf(lrow[k] - mx);
-  se = wave_sum(se);
-  const float inv = 1.f / se;
-  const float logse = logf(se);
+  // logits: p = softmax over the K entries (shifted by the row maximum);
+  // log-probabilities: p = exp(entry) as given (mass M may be below one)
+  float mx = 0.f, inv = 1.f, logse = 0.f;
+  if (!logprob) {
+    mx = -INFINITY;
+    for (int k = lane; k < K; k += 64) mx = fmaxf(mx, lrow[k]);
+    mx = wave_max(mx);
+    float se = 0.f;
+    for (int k = lane; k < K; k += 64) se += expf(lrow[k] - mx);
+    se = wave_sum(se);
+    inv = 1.f / se;
+    logse = logf(se);
+  }
   float ent = 0.f, mass = 0.f;
   for (int k = lane; k < Kp; k += 64) {
     if (k < K) {
       const float a = lrow[k] - mx;
       const float p = expf(a) * inv;
-      ent += p * (a - logse);
+      if (p > 0.f) ent += p * (a - logse);  // p log p, with 0 log 0 = 0
       mass += p;
       key[k] = irow[k];
       val[k] = p;
@@ -795,16 +800,18 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
 // contraction spends on double-buffered fragments.  fp32 (small problems):
 // 128 x 128 tiles, register-staged loads.
 using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 0>;
+using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
 using CfgBF16Gemm = Dma64Cfg<256, 256, 128, 64, 1>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
 template <typename TIn>
 struct CfgOf;
 template <>
-struct CfgOf<bf16_t> { using type = CfgBF16; using gemm = CfgBF16Gemm; };
+struct CfgOf<bf16_t> { using type = CfgBF16; using bwd = CfgBF16Bwd; using gemm = CfgBF16Gemm; };
 template <>
-struct CfgOf<float> { using type = CfgF32; using gemm = CfgF32; };
-static_assert(CfgBF16::BM == CfgBF16Gemm::BM && CfgBF16::BN == CfgBF16Gemm::BN, "one tile size per dtype");
+struct CfgOf<float> { using type = CfgF32; using bwd = CfgF32; using gemm = CfgF32; };
+static_assert(CfgBF16::BM == CfgBF16Gemm::BM && CfgBF16::BN == CfgBF16Gemm::BN && CfgBF16::BM == CfgBF16Bwd::BM &&
+                  CfgBF16::BN == CfgBF16Bwd::BN, "one tile size per dtype");
 
 #define CKL_LAUNCH_CHECK() \
   do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
@@ -837,12 +844,12 @@ hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const i
 }
 
 hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
-                               float* Erow, float* Mrow, float* zg_s, int* bad, hipStream_t st) {
+                               float* Erow, float* Mrow, float* zg_s, int* bad, int logprob, hipStream_t st) {
   int Kp = 64;
   while (Kp < K) Kp <<= 1;
   const size_t lds = (size_t)Kp * 8;
   hipLaunchKernelGGL(teacher_prep_kernel, dim3(T), dim3(64), lds, st, idx, tlogit, T, K, Kp, V, idx_s, p_s, Erow,
-                     Mrow, zg_s, bad);
+                     Mrow, zg_s, bad, logprob);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -925,7 +932,7 @@ static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, 
                              const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
                              int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G,
                              int64_t ldG, void* Gt, int64_t ldGt, hipStream_t st) {
-  using C = typename CfgOf<TIn>::type;
+  using C = typename CfgOf<TIn>::bwd;
   const int n_vtiles = v_rows / C::BM;
   const int n_tblocks = t_rows / C::BN;
   hipLaunchKernelGGL(bwd_grad_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,

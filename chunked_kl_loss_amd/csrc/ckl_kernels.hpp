@@ -11,8 +11,10 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_count_mask(const uint8_t* mask, int T, int* N, hipStream_t st);
 hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const int* N, int T, int Tp, float* s,
                             hipStream_t st);
+// logprob = 0: tlogit holds logits (softmax over the K entries); 1: it holds
+// log-probabilities, used as given.
 hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
-                               float* Erow, float* Mrow, float* zg_s, int* bad, hipStream_t st);
+                               float* Erow, float* Mrow, float* zg_s, int* bad, int logprob, hipStream_t st);
 // G == nullptr: log-sum-exp partials only.  Otherwise also the exponentials
 // u (G, row stride ldG) and the per-tile maxima (mtab, row stride ldm) of the
 // fused forward + backward.

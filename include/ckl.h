@@ -6,7 +6,9 @@
  * weights W[V, d] and, for every row t, a sparse cached teacher made of K
  * vocabulary indices idx[t, :] and their logits tlogit[t, :], the library
  * evaluates the forward KL divergence KL(p_t || q_t) between
- *   p_t = softmax over the K cached logits (temperature 1), zero elsewhere,
+ *   p_t = softmax over the K cached logits (temperature 1), zero elsewhere
+ *         (or, with teacher_form = CKL_TEACHER_LOGPROBS, the cached
+ *         log-probabilities exponentiated as given),
  *   q_t = softmax(z_t) with z_t = W h_t (full vocabulary),
  * in the sparse form given in the objective section of the README page
  * "Chunked KL loss, running Knowledge Distillation locally in less <6GB VRAM":
@@ -71,10 +73,19 @@ typedef enum {
 
 typedef enum { CKL_F32 = 0, CKL_BF16 = 1 } ckl_dtype;
 
+/* What the K cached teacher values of a row are (the objective section of the
+ * README page carries the teacher mass M explicitly):
+ *   CKL_TEACHER_LOGITS:   logits; p = softmax over the K entries (M = 1).
+ *   CKL_TEACHER_LOGPROBS: the teacher's own log-probabilities over its full
+ *                         vocabulary, truncated to the top K and used as
+ *                         given: p = exp(value), M = sum_k p_k (may be < 1;
+ *                         -inf entries are zero-probability tokens). */
+typedef enum { CKL_TEACHER_LOGITS = 0, CKL_TEACHER_LOGPROBS = 1 } ckl_teacher_form;
+
 typedef struct {
-  int64_t T;      /* rows (batch x sequence, flattened), >= 1              */
+  int64_t T;      /* rows (batch x sequence, flattened), 1 .. 4,000,000    */
   int64_t d;      /* hidden size, >= 8 and a multiple of 8                 */
-  int64_t V;      /* vocabulary size, >= 1                                 */
+  int64_t V;      /* vocabulary size, 1 .. 4,000,000                       */
   int64_t K;      /* teacher entries per row, 1 <= K <= min(V, 4096)       */
   int64_t chunk;  /* backward G-block budget in rows of V entries, >= 1:   */
                   /* the backward keeps at most about chunk*V logit        */
@@ -88,6 +99,7 @@ typedef struct {
                      /* entries never cause an out-of-bounds access (they  */
                      /* match no vocabulary column) but the result is then */
                      /* undefined, as it is for repeated entries.          */
+  int32_t teacher_form; /* ckl_teacher_form of tlogit (0 = logits)         */
 } ckl_problem;
 
 /* Workspace bytes needed by ckl_forward (which = 0), ckl_backward

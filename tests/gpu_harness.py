@@ -36,7 +36,7 @@ def to_device(x, device="cuda"):
 
 
 def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False,
-            want_grads=True):
+            want_grads=True, teacher_form=0):
     """Forward + backward through the C ABI.  Returns float64 numpy results."""
     import torch
 
@@ -45,12 +45,13 @@ def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="in
     if not isinstance(mask, str):
         m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=np.uint8)).cuda()
     chunk = x.chunk if chunk is None else chunk
-    loss, lse, row_loss = ckl.forward(H, W, idx, tl, m, chunk=chunk, validate=validate, want_row_loss=True)
+    loss, lse, row_loss = ckl.forward(H, W, idx, tl, m, chunk=chunk, validate=validate, want_row_loss=True,
+                                      teacher_form=teacher_form)
     out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy())
     if want_grads:
         g = torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
         dH, dW = ckl.backward(H, W, idx, tl, m, lse, g, chunk=chunk, dh_dtype=dh_dtype, dw_dtype=dw_dtype,
-                              validate=validate)
+                              validate=validate, teacher_form=teacher_form)
         torch.cuda.synchronize()
         out["dH"] = dH.double().cpu().numpy()
         out["dW"] = dW.double().cpu().numpy()
@@ -59,7 +60,8 @@ def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="in
     return out
 
 
-def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False):
+def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False,
+                  teacher_form=0):
     """The one-call forward + backward (no logit recompute) through the C ABI."""
     import torch
 
@@ -70,7 +72,8 @@ def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, ma
     chunk = x.chunk if chunk is None else chunk
     g = None if grad_loss is None else torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
     loss, lse, row_loss, dH, dW = ckl.forward_backward(H, W, idx, tl, m, g, chunk=chunk, dh_dtype=dh_dtype,
-                                                       dw_dtype=dw_dtype, validate=validate, want_row_loss=True)
+                                                       dw_dtype=dw_dtype, validate=validate, want_row_loss=True,
+                                                       teacher_form=teacher_form)
     torch.cuda.synchronize()
     out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy(),
                dH=dH.double().cpu().numpy(), dW=dW.double().cpu().numpy())

@@ -58,6 +58,10 @@ def _prob(**kw):
     (dict(chunk=0), B.CKL_ERR_INVALID_ARG),
     (dict(in_dtype=7), B.CKL_ERR_INVALID_ARG),
     (dict(d=131072), B.CKL_ERR_UNSUPPORTED),
+    (dict(T=4000001), B.CKL_ERR_UNSUPPORTED),
+    (dict(teacher_form=2), B.CKL_ERR_INVALID_ARG),
+    (dict(teacher_form=-1), B.CKL_ERR_INVALID_ARG),
+    (dict(V=4000001), B.CKL_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(lib, kw, status):
     p = _prob(**kw)

@@ -17,7 +17,7 @@ import pytest
 import oracle
 from synth import make_inputs
 from tests.gpu_harness import TOL, max_rel, run_gpu, run_gpu_fused, say
-from tests.test_parity_gpu import _custom, check_full, oracle_full
+from tests.test_parity_gpu import _custom, check_full, oracle_full, with_logprob_teacher
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +173,14 @@ def test_fused_autograd_function():
     assert H.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
     assert max_rel(H.grad.double().cpu().numpy(), ref["dH"]) <= 1e-2
     assert max_rel(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-2
+
+
+def test_fused_logprob_teacher():
+    x = with_logprob_teacher(inputs(0), n_neg_inf=5)
+    say(f"case fused log-prob teacher fp32 T={x.T}")
+    got = run_gpu_fused(x, teacher_form=1, grad_loss=0.6)
+    check_full(x, got, oracle_full(x, grad_loss=0.6, teacher_form=1), TOL["f32"], 1e-5)
+    y = with_logprob_teacher(inputs(2, T=1000))
+    say(f"case fused log-prob teacher cfg2 slice T={y.T}")
+    got = run_gpu_fused(y, teacher_form=1)
+    check_full(y, got, oracle_full(y, teacher_form=1), TOL["bf16"], 2e-3)

@@ -46,9 +46,26 @@ def check_full(x, got, ref, tol, lse_tol):
     return e_h, e_w
 
 
-def oracle_full(x, grad_loss=1.0, mask="inputs"):
+def oracle_full(x, grad_loss=1.0, mask="inputs", teacher_form=0):
     m = x.mask if isinstance(mask, str) else mask
-    return oracle.kl_dense(x.H, x.W, x.idx, x.tlogit, mask=m, grad_loss=grad_loss, block=128)
+    return oracle.kl_dense(x.H, x.W, x.idx, x.tlogit, mask=m, grad_loss=grad_loss, block=128,
+                           teacher_form=teacher_form)
+
+
+def with_logprob_teacher(x, seed=31, extra=400, n_neg_inf=0):
+    """The same problem with the K cached values replaced by the top-K
+    log-probabilities of a teacher over K + extra classes (teacher mass below
+    one), optionally with some -inf entries (zero-probability tokens)."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    full = rng.normal(0.0, 2.0, size=(x.T, x.K + extra))
+    full -= full.max(axis=1, keepdims=True)
+    full -= np.log(np.exp(full).sum(axis=1, keepdims=True))
+    lp = np.sort(full, axis=1)[:, ::-1][:, :x.K].astype(np.float32)
+    if n_neg_inf:
+        rows = rng.choice(x.T, size=n_neg_inf, replace=False)
+        lp[rows, -1] = -np.inf
+    return dataclasses.replace(x, tlogit=np.ascontiguousarray(lp))
 
 
 # ------------------------------------------------------------- full parity --
@@ -201,3 +218,19 @@ def test_autograd_function():
     assert H.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
     assert max_rel(H.grad.double().cpu().numpy(), ref["dH"]) <= 1e-2
     assert max_rel(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-2
+
+
+# ------------------------------------------- teacher given as log-probs ----
+def test_logprob_teacher_fp32_full():
+    x = with_logprob_teacher(inputs(0), n_neg_inf=5)
+    assert np.exp(x.tlogit.astype(np.float64)).sum(axis=1).max() < 0.99
+    say(f"case log-prob teacher fp32 T={x.T} V={x.V} K={x.K}")
+    got = run_gpu(x, teacher_form=1, grad_loss=0.6)
+    check_full(x, got, oracle_full(x, grad_loss=0.6, teacher_form=1), TOL["f32"], 1e-5)
+
+
+def test_logprob_teacher_bf16_large_vocab():
+    x = with_logprob_teacher(inputs(4, T=677))
+    say(f"case log-prob teacher cfg4 slice T={x.T} masked={x.mask is not None}")
+    got = run_gpu(x, teacher_form=1, chunk=300)
+    check_full(x, got, oracle_full(x, teacher_form=1), TOL["bf16"], 2e-3)
