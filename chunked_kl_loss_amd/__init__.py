@@ -24,6 +24,8 @@ from ._binding import (  # noqa: F401
     fused_plan,
     load_library,
     make_problem,
+    shard_combine,
+    shard_forward,
     timing_enable,
     timing_read,
     workspace_size,

@@ -30,6 +30,8 @@ EXPORTED = (
     "ckl_backward_plan",
     "ckl_forward_backward",
     "ckl_fused_plan",
+    "ckl_shard_forward",
+    "ckl_shard_combine",
     "ckl_timing_enable",
     "ckl_timing_read",
     "ckl_status_string",
@@ -56,6 +58,8 @@ class Problem(ctypes.Structure):
         ("dw_dtype", ctypes.c_int32),
         ("validate", ctypes.c_int32),
         ("teacher_form", ctypes.c_int32),
+        ("v_offset", ctypes.c_int64),
+        ("v_total", ctypes.c_int64),
     ]
 
 
@@ -86,6 +90,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckl_forward_backward.restype = i32
     lib.ckl_fused_plan.argtypes = [P, i64p]
     lib.ckl_fused_plan.restype = i32
+    lib.ckl_shard_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ckl_shard_forward.restype = i32
+    lib.ckl_shard_combine.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ckl_shard_combine.restype = i32
     lib.ckl_timing_enable.argtypes = [ctypes.c_int]
     lib.ckl_timing_enable.restype = i32
     lib.ckl_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), i64p]
@@ -108,10 +116,10 @@ def check(status: int, lib=None) -> None:
 
 
 def make_problem(T, d, V, K, chunk, in_dtype=CKL_BF16, dh_dtype=None, dw_dtype=CKL_F32, validate=False,
-                 teacher_form=CKL_TEACHER_LOGITS) -> Problem:
+                 teacher_form=CKL_TEACHER_LOGITS, v_offset=0, v_total=0) -> Problem:
     return Problem(int(T), int(d), int(V), int(K), int(chunk), int(in_dtype),
                    int(in_dtype if dh_dtype is None else dh_dtype), int(dw_dtype), int(bool(validate)),
-                   int(teacher_form))
+                   int(teacher_form), int(v_offset), int(v_total))
 
 
 def workspace_size(prob: Problem, which: int) -> int:
@@ -227,7 +235,8 @@ def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = Fa
 
 
 def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh_dtype=None,
-             dw_dtype=None, validate: bool = False, teacher_form: int = CKL_TEACHER_LOGITS):
+             dw_dtype=None, validate: bool = False, teacher_form: int = CKL_TEACHER_LOGITS,
+             v_offset: int = 0, v_total: int = 0):
     """Returns (dH, dW) of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
@@ -236,7 +245,7 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     in_code = _dtype_code(H.dtype)
     dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
     dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
-    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form, v_offset, v_total)
     lib = load_library()
     ws_bytes = workspace_size(prob, 1)
     dev = H.device
@@ -280,3 +289,48 @@ def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 
                                    _ptr(grad_loss), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(dH), _ptr(dW),
                                    _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
     return loss, lse, row_loss, dH, dW
+
+
+def shard_forward(H, W_shard, idx, tlogit, v_offset: int, v_total: int, chunk: int = 2048,
+                  validate: bool = False, teacher_form: int = CKL_TEACHER_LOGITS):
+    """One vocabulary shard (rows [v_offset, v_offset + W_shard.shape[0]) of a v_total-row head):
+    returns (lse_part [T], cross_part [T]) float32."""
+    torch = _torch()
+    _check_inputs(H, W_shard, idx, tlogit, None)
+    T, d = H.shape
+    V, K = W_shard.shape[0], idx.shape[1]
+    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate, teacher_form=teacher_form,
+                        v_offset=v_offset, v_total=v_total)
+    lib = load_library()
+    ws_bytes = workspace_size(prob, 0)
+    dev = H.device
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    lse_part = torch.empty(T, dtype=torch.float32, device=dev)
+    cross_part = torch.empty(T, dtype=torch.float32, device=dev)
+    check(lib.ckl_shard_forward(ctypes.byref(prob), _ptr(H), _ptr(W_shard), _ptr(idx), _ptr(tlogit),
+                                _ptr(lse_part), _ptr(cross_part), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
+    return lse_part, cross_part
+
+
+def shard_combine(lse_parts, cross_parts, idx, tlogit, mask=None, v_total: int = 1, d: int = 8,
+                  teacher_form: int = CKL_TEACHER_LOGITS, want_row_loss: bool = False):
+    """Merge [n_shards, T] partials: returns (loss [1], lse [T], row_loss [T] or None)."""
+    torch = _torch()
+    n_shards, T = lse_parts.shape
+    K = idx.shape[1]
+    for name, t in (("lse_parts", lse_parts), ("cross_parts", cross_parts), ("idx", idx), ("tlogit", tlogit)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    prob = make_problem(T, d, v_total, K, 1, CKL_F32, teacher_form=teacher_form)
+    lib = load_library()
+    ws_bytes = workspace_size(prob, 3)
+    dev = lse_parts.device
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    m = mask.view(torch.uint8) if mask is not None else None
+    check(lib.ckl_shard_combine(ctypes.byref(prob), int(n_shards), _ptr(lse_parts), _ptr(cross_parts), _ptr(idx),
+                                _ptr(tlogit), _ptr(m), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws_bytes,
+                                _stream_ptr(dev)), lib)
+    return loss, lse, row_loss

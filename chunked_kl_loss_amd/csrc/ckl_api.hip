@@ -147,6 +147,10 @@ void pick_splits(int64_t row_blocks, int64_t vtiles, int64_t* splits, int64_t* t
   }
 }
 
+// Full vocabulary size (v_total = 0: W holds all of it).
+int64_t vtotal(const ckl_problem* p) { return p->v_total ? p->v_total : p->V; }
+bool sharded(const ckl_problem* p) { return p->v_offset != 0 || vtotal(p) != p->V; }
+
 ckl_status check_problem(const ckl_problem* p) {
   if (!p) return fail(CKL_ERR_INVALID_ARG, "problem is NULL");
   if (p->T < 1) return fail(CKL_ERR_INVALID_ARG, "T=%lld must be >= 1", (long long)p->T);
@@ -156,7 +160,13 @@ ckl_status check_problem(const ckl_problem* p) {
                 (long long)kMaxRows);
   if (p->d < 8 || p->d % 8 != 0) return fail(CKL_ERR_INVALID_ARG, "d=%lld must be a positive multiple of 8", (long long)p->d);
   if (p->d > 65536) return fail(CKL_ERR_UNSUPPORTED, "d=%lld exceeds 65536", (long long)p->d);
-  if (p->K < 1 || p->K > p->V) return fail(CKL_ERR_INVALID_ARG, "K=%lld must satisfy 1 <= K <= V", (long long)p->K);
+  if (p->v_offset < 0 || p->v_total < 0) return fail(CKL_ERR_INVALID_ARG, "v_offset and v_total must be >= 0");
+  if (vtotal(p) < p->v_offset + p->V)
+    return fail(CKL_ERR_INVALID_ARG, "v_offset + V = %lld exceeds v_total = %lld", (long long)(p->v_offset + p->V),
+                (long long)vtotal(p));
+  if (vtotal(p) >= ((int64_t)1 << 31)) return fail(CKL_ERR_UNSUPPORTED, "v_total must stay below 2^31 (int32 idx)");
+  if (p->K < 1 || p->K > vtotal(p))
+    return fail(CKL_ERR_INVALID_ARG, "K=%lld must satisfy 1 <= K <= v_total", (long long)p->K);
   if (p->K > kMaxK) return fail(CKL_ERR_UNSUPPORTED, "K=%lld exceeds %lld", (long long)p->K, (long long)kMaxK);
   if (p->T * p->K >= ((int64_t)1 << 31)) return fail(CKL_ERR_UNSUPPORTED, "T*K must stay below 2^31");
   if (p->chunk < 1) return fail(CKL_ERR_INVALID_ARG, "chunk=%lld must be >= 1", (long long)p->chunk);
@@ -290,6 +300,24 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   return w;
 }
 
+struct CombineWs {
+  size_t idx_s, p_s, E, M, blk, N, bad, total;
+};
+CombineWs combine_layout(const Plan& q) {
+  CombineWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+  w.idx_s = take(q.T * q.K * 4);
+  w.p_s = take(q.T * q.K * 4);
+  w.E = take(q.T * 4);
+  w.M = take(q.T * 4);
+  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.N = take(4);
+  w.bad = take(4);
+  w.total = o;
+  return w;
+}
+
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 ckl_status check_validate_flag(int* bad_dev, hipStream_t st) {
@@ -308,10 +336,14 @@ ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
   if (!bytes) return fail(CKL_ERR_INVALID_ARG, "bytes is NULL");
-  if (which < 0 || which > 2)
-    return fail(CKL_ERR_INVALID_ARG, "which must be 0 (forward), 1 (backward) or 2 (forward + backward)");
+  if (which < 0 || which > 3)
+    return fail(CKL_ERR_INVALID_ARG,
+                "which must be 0 (forward, shard forward), 1 (backward), 2 (forward + backward) or 3 (shard combine)");
   const Plan q = make_plan(p);
-  *bytes = which == 0 ? fwd_layout(q).total : which == 1 ? bwd_layout(q, p).total : fused_layout(q, p).total;
+  *bytes = which == 0   ? fwd_layout(q).total
+           : which == 1 ? bwd_layout(q, p).total
+           : which == 2 ? fused_layout(q, p).total
+                        : combine_layout(q).total;
   return CKL_OK;
 }
 
@@ -320,6 +352,8 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
                        void* stream) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
+  if (sharded(p))
+    return fail(CKL_ERR_UNSUPPORTED, "W is a vocabulary shard: use ckl_shard_forward and ckl_shard_combine");
   if (!H || !W || !idx || !tlogit || !loss || !lse) return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(ws))
     return fail(CKL_ERR_INVALID_ARG, "H, W, idx, tlogit and ws must be 16-byte aligned");
@@ -344,7 +378,7 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
-                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, E, M, zg_s,
                                                   p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
@@ -406,7 +440,7 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
-                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, nullptr, M, nullptr,
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, nullptr, M, nullptr,
                                                   p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
@@ -467,6 +501,8 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
                                 void* stream) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
+  if (sharded(p))
+    return fail(CKL_ERR_UNSUPPORTED, "W is a vocabulary shard: the one-call path needs the whole vocabulary");
   if (!H || !W || !idx || !tlogit || !loss || !lse || !dH || !dW)
     return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(dH) || !aligned16(dW) ||
@@ -504,7 +540,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
-                  return ckl::launch_teacher_prep(idx, tlogit, T, K, V, idx_s, p_s, E, M, zg_s,
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, E, M, zg_s,
                                                   p->validate ? bad : nullptr, p->teacher_form, st);
                 }),
           "teacher_prep");
@@ -579,6 +615,96 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   return CKL_OK;
 }
 
+ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W, const int32_t* idx,
+                             const float* tlogit, float* lse_part, float* cross_part, void* ws, size_t ws_bytes,
+                             void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (!H || !W || !idx || !tlogit || !lse_part || !cross_part)
+    return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(H) || !aligned16(W) || !aligned16(idx) || !aligned16(tlogit) || !aligned16(ws))
+    return fail(CKL_ERR_INVALID_ARG, "H, W, idx, tlogit and ws must be 16-byte aligned");
+  if (((uintptr_t)lse_part & 3u) || ((uintptr_t)cross_part & 3u))
+    return fail(CKL_ERR_INVALID_ARG, "lse_part and cross_part must be 4-byte aligned");
+  const Plan q = make_plan(p);
+  const FwdWs w = fwd_layout(q);
+  if (!ws || ws_bytes < w.total)
+    return fail(CKL_ERR_WORKSPACE, "shard forward workspace needs %zu bytes, got %zu", w.total,
+                ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* b = (char*)ws;
+  int* idx_s = (int*)(b + w.idx_s);
+  float* p_s = (float*)(b + w.p_s);
+  float* zg_s = (float*)(b + w.zg_s);
+  int* bad = (int*)(b + w.bad);
+  const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
+  if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
+  HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
+                [&] {
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s,
+                                                  (float*)(b + w.E), (float*)(b + w.M), zg_s,
+                                                  p->validate ? bad : nullptr, p->teacher_form, st);
+                }),
+          "teacher_prep");
+  if (p->validate) {
+    s = check_validate_flag(bad, st);
+    if (s != CKL_OK) return s;
+  }
+  HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
+                [&] {
+                  return ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits,
+                                             (int)q.f_tps, nullptr, 0, nullptr, 0, st);
+                }),
+          "fwd_lse");
+  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                [&] {
+                  return ckl::launch_fwd_shard_rows(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, lse_part,
+                                                    cross_part, st);
+                }),
+          "fwd_shard_rows");
+  return CKL_OK;
+}
+
+ckl_status ckl_shard_combine(const ckl_problem* p, int32_t n_shards, const float* lse_parts,
+                             const float* cross_parts, const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                             float* loss, float* lse, float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (n_shards < 1) return fail(CKL_ERR_INVALID_ARG, "n_shards=%d must be >= 1", (int)n_shards);
+  if (!lse_parts || !cross_parts || !idx || !tlogit || !loss || !lse)
+    return fail(CKL_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(idx) || !aligned16(tlogit) || !aligned16(ws))
+    return fail(CKL_ERR_INVALID_ARG, "idx, tlogit and ws must be 16-byte aligned");
+  if (((uintptr_t)lse_parts & 3u) || ((uintptr_t)cross_parts & 3u) || ((uintptr_t)loss & 3u) ||
+      ((uintptr_t)lse & 3u) || ((uintptr_t)row_loss & 3u))
+    return fail(CKL_ERR_INVALID_ARG, "float arrays must be 4-byte aligned");
+  const Plan q = make_plan(p);
+  const CombineWs w = combine_layout(q);
+  if (!ws || ws_bytes < w.total)
+    return fail(CKL_ERR_WORKSPACE, "shard combine workspace needs %zu bytes, got %zu", w.total,
+                ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* b = (char*)ws;
+  int* N = (int*)(b + w.N);
+  const int T = (int)q.T, K = (int)q.K;
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
+                [&] {
+                  return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), 0, (int*)(b + w.idx_s),
+                                                  (float*)(b + w.p_s), (float*)(b + w.E), (float*)(b + w.M), nullptr,
+                                                  nullptr, p->teacher_form, st);
+                }),
+          "teacher_prep");
+  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                [&] {
+                  return ckl::launch_shard_combine(lse_parts, cross_parts, (int)n_shards, T, (float*)(b + w.E),
+                                                   (float*)(b + w.M), mask, lse, row_loss, (double*)(b + w.blk), N,
+                                                   loss, st);
+                }),
+          "shard_combine");
+  return CKL_OK;
+}
+
 ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
@@ -641,6 +767,6 @@ const char* ckl_status_string(ckl_status s) {
 
 const char* ckl_last_error(void) { return g_last_error.c_str(); }
 
-int32_t ckl_version(void) { return (1 << 16) | 1; }
+int32_t ckl_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

@@ -114,7 +114,7 @@ __global__ void row_scale_kernel(const uint8_t* __restrict__ mask, const float* 
 // bitonic sort of (idx, p) by idx in LDS.  Optional outputs: E (sum p log p),
 // zero-filled zg.  `bad` collects out-of-range / repeated indices.
 __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict__ idx, const float* __restrict__ tlogit,
-                                                          int T, int K, int Kp, int V, int* __restrict__ idx_s,
+                                                          int T, int K, int Kp, int V, int voff, int* __restrict__ idx_s,
                                                           float* __restrict__ p_s, float* __restrict__ Erow,
                                                           float* __restrict__ Mrow, float* __restrict__ zg_s,
                                                           int* __restrict__ bad, int logprob) {
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
   int badl = 0;
   for (int k = lane; k < K; k += 64) {
     const int v = key[k];
-    idx_s[(int64_t)t * K + k] = v;
+    idx_s[(int64_t)t * K + k] = v - voff;  // vocabulary row of this shard's W (out of range: another shard's)
     p_s[(int64_t)t * K + k] = val[k];
     if (zg_s) zg_s[(int64_t)t * K + k] = 0.f;
     if (v < 0 || v >= V || (k + 1 < K && key[k + 1] == v)) badl = 1;
@@ -387,6 +387,72 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const double* __restri
     const int n = *N;
     *loss = n > 0 ? (float)(red[0] / (double)n) : 0.f;
   }
+}
+
+// ------------------------------------------------ vocabulary shards --
+// One thread per row: the shard's natural-log LSE over its vocabulary rows
+// (split states merged) and its share of the cross term, sum over the
+// teacher entries that fall in the shard of p * z (fp64 sum).
+__global__ __launch_bounds__(256) void fwd_shard_rows_kernel(const float2* __restrict__ part, int S, int T, int K,
+                                                             const float* __restrict__ p_s,
+                                                             const float* __restrict__ zg_s,
+                                                             float* __restrict__ lse_part,
+                                                             float* __restrict__ cross_part) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  float m = -INFINITY, s = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float2 x = part[(int64_t)sp * T + t];
+    lse2_merge(m, s, x.x, x.y);
+  }
+  lse_part[t] = (m + fast_log2(s)) * kLn2;
+  double x = 0.0;
+  const float* pr = p_s + (int64_t)t * K;
+  const float* zr = zg_s + (int64_t)t * K;
+  for (int k = 0; k < K; ++k) x += (double)pr[k] * (double)zr[k];
+  cross_part[t] = (float)x;
+}
+
+// One thread per row: merge the shards' partial LSE (fp64 log-sum-exp of the
+// natural-log partials) and cross terms into LSE and l_t = E - sum cross +
+// M LSE; masked rows give 0; per-256-row fp64 sums as in fwd_finalize.
+__global__ __launch_bounds__(256) void shard_combine_kernel(const float* __restrict__ lse_parts,
+                                                            const float* __restrict__ cross_parts, int S, int T,
+                                                            const float* __restrict__ Erow,
+                                                            const float* __restrict__ Mrow,
+                                                            const uint8_t* __restrict__ mask,
+                                                            float* __restrict__ lse_out, float* __restrict__ row_loss,
+                                                            double* __restrict__ blk_sum) {
+  __shared__ double red[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  if (t < T) {
+    const bool keep = mask == nullptr || mask[t] != 0;
+    float lse = 0.f, l = 0.f;
+    if (keep) {
+      double m = -INFINITY;
+      for (int sh = 0; sh < S; ++sh) m = fmax(m, (double)lse_parts[(int64_t)sh * T + t]);
+      double sum = 0.0, cross = 0.0;
+      for (int sh = 0; sh < S; ++sh) {
+        sum += exp((double)lse_parts[(int64_t)sh * T + t] - m);
+        cross += (double)cross_parts[(int64_t)sh * T + t];
+      }
+      const double L = m + log(sum);
+      const double ld = (double)Erow[t] - cross + (double)Mrow[t] * L;
+      lse = (float)L;
+      l = (float)ld;
+      contrib = ld;
+    }
+    lse_out[t] = lse;
+    if (row_loss) row_loss[t] = l;
+  }
+  red[threadIdx.x] = contrib;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blk_sum[blockIdx.x] = red[0];
 }
 
 // ----------------------------------------------------- transposes / casts --
@@ -843,13 +909,14 @@ hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const i
   return hipSuccess;
 }
 
-hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
-                               float* Erow, float* Mrow, float* zg_s, int* bad, int logprob, hipStream_t st) {
+hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int voff, int* idx_s,
+                               float* p_s, float* Erow, float* Mrow, float* zg_s, int* bad, int logprob,
+                               hipStream_t st) {
   int Kp = 64;
   while (Kp < K) Kp <<= 1;
   const size_t lds = (size_t)Kp * 8;
-  hipLaunchKernelGGL(teacher_prep_kernel, dim3(T), dim3(64), lds, st, idx, tlogit, T, K, Kp, V, idx_s, p_s, Erow,
-                     Mrow, zg_s, bad, logprob);
+  hipLaunchKernelGGL(teacher_prep_kernel, dim3(T), dim3(64), lds, st, idx, tlogit, T, K, Kp, V, voff, idx_s, p_s,
+                     Erow, Mrow, zg_s, bad, logprob);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -905,6 +972,24 @@ hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const floa
   hipError_t e = launch_fwd_rows(part, S, T, K, p_s, zg_s, Erow, Mrow, mask, lse, row_loss, blk_sum, st);
   if (e != hipSuccess) return e;
   return launch_loss_reduce(blk_sum, (T + 255) / 256, N, loss, st);
+}
+
+hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
+                                 float* lse_part, float* cross_part, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_shard_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, st, (const float2*)part, S, T, K, p_s,
+                     zg_s, lse_part, cross_part);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_shard_combine(const float* lse_parts, const float* cross_parts, int S, int T, const float* Erow,
+                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* blk_sum,
+                                const int* N, float* loss, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  hipLaunchKernelGGL(shard_combine_kernel, dim3(nblk), dim3(256), 0, st, lse_parts, cross_parts, S, T, Erow, Mrow,
+                     mask, lse, row_loss, blk_sum);
+  CKL_LAUNCH_CHECK();
+  return launch_loss_reduce(blk_sum, nblk, N, loss, st);
 }
 
 hipError_t launch_transpose_pad(int in_bf16, const void* src, int R, int C, int Rp, void* dst, int64_t ldd,

@@ -12,9 +12,18 @@ hipError_t launch_count_mask(const uint8_t* mask, int T, int* N, hipStream_t st)
 hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const int* N, int T, int Tp, float* s,
                             hipStream_t st);
 // logprob = 0: tlogit holds logits (softmax over the K entries); 1: it holds
-// log-probabilities, used as given.
-hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int* idx_s, float* p_s,
-                               float* Erow, float* Mrow, float* zg_s, int* bad, int logprob, hipStream_t st);
+// log-probabilities, used as given.  Indices are checked against [0, V) and
+// stored sorted, minus voff (the first vocabulary row of this shard's W).
+hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int voff, int* idx_s,
+                               float* p_s, float* Erow, float* Mrow, float* zg_s, int* bad, int logprob,
+                               hipStream_t st);
+// Vocabulary shards: per-row partial LSE and cross term of one shard; and the
+// merge of S shards' partials ([S][T] each) into LSE, row loss and the mean.
+hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
+                                 float* lse_part, float* cross_part, hipStream_t st);
+hipError_t launch_shard_combine(const float* lse_parts, const float* cross_parts, int S, int T, const float* Erow,
+                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* blk_sum,
+                                const int* N, float* loss, hipStream_t st);
 // G == nullptr: log-sum-exp partials only.  Otherwise also the exponentials
 // u (G, row stride ldG) and the per-tile maxima (mtab, row stride ldm) of the
 // fused forward + backward.

@@ -100,12 +100,17 @@ typedef struct {
                      /* match no vocabulary column) but the result is then */
                      /* undefined, as it is for repeated entries.          */
   int32_t teacher_form; /* ckl_teacher_form of tlogit (0 = logits)         */
+  int64_t v_offset;  /* vocabulary shards: W holds vocabulary rows           */
+  int64_t v_total;   /* [v_offset, v_offset + V) of a vocabulary of v_total */
+                     /* (0 = V: W is the whole head).  idx holds ids in     */
+                     /* [0, v_total); K <= v_total.  Only ckl_shard_forward,*/
+                     /* ckl_shard_combine and ckl_backward accept a shard.  */
 } ckl_problem;
 
-/* Workspace bytes needed by ckl_forward (which = 0), ckl_backward
- * (which = 1) or ckl_forward_backward (which = 2) for problem *p.  Writes
- * *bytes; returns CKL_OK or CKL_ERR_INVALID_ARG / CKL_ERR_UNSUPPORTED for a
- * bad problem. */
+/* Workspace bytes needed by ckl_forward or ckl_shard_forward (which = 0),
+ * ckl_backward (which = 1), ckl_forward_backward (which = 2) or
+ * ckl_shard_combine (which = 3) for problem *p.  Writes *bytes; returns
+ * CKL_OK or CKL_ERR_INVALID_ARG / CKL_ERR_UNSUPPORTED for a bad problem. */
 ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes);
 
 /* Forward pass: loss, per-row log-sum-exp and per-row KL.
@@ -124,7 +129,9 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* Backward pass: dH and dW of grad_loss * loss.
- *   lse:       [T] from ckl_forward on the same inputs.
+ *   lse:       [T] from ckl_forward on the same inputs (or from
+ *              ckl_shard_combine; on a vocabulary shard dW is the shard's
+ *              rows and dH its contribution to the sum over shards).
  *   grad_loss: [1] device float32 or NULL (= 1).
  *   dH, dW:    outputs, overwritten (not accumulated into).
  *   ws:        device workspace of at least ckl_workspace_size(p, 1) bytes.
@@ -180,6 +187,40 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
  * chunk, out[1] = number of chunks, out[2] = number of dH split-k parts,
  * out[3] = vocabulary columns per part.  Host-only; touches no device. */
 ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]);
+
+/* Vocabulary-parallel shards (the README usage table's tensor-parallel
+ * option shards the output head; the pages do not describe the exchange).
+ * With W split by rows over P devices, only the log-normaliser and the cross
+ * term need the whole vocabulary, and both merge from per-shard partials:
+ *   1. every shard: ckl_shard_forward(p with v_offset / v_total, its W rows)
+ *      -> lse_part[t]  = log sum over the shard's rows of exp(z_t[v]),
+ *         cross_part[t] = sum over the teacher entries of row t that fall in
+ *                         the shard of p_tk z_t[idx_tk];
+ *   2. gather the P partials of every row (an all-gather of T x 8 bytes per
+ *      device) and ckl_shard_combine them into loss, lse and row_loss;
+ *   3. every shard: ckl_backward(p with the same v_offset / v_total, its W
+ *      rows, the combined lse) -> dW rows of the shard and that shard's
+ *      contribution to dH; the sum of dH over the shards (an all-reduce) is
+ *      the gradient.
+ * On one device the shards can be run in turn.  Partials are fp32 (the
+ * cross term summed in fp64 per shard; the merge in fp64).
+ *
+ * ckl_shard_forward: lse_part, cross_part are [T] device float32, written for
+ * every row (masks apply in the combine).  ws: ckl_workspace_size(p, 0).
+ * ckl_shard_combine: lse_parts and cross_parts are [n_shards, T] device
+ * float32 (shard-major); idx and tlogit as given to the shards (the teacher
+ * entropy and mass are recomputed); loss, lse, row_loss as in ckl_forward.
+ * ws: ckl_workspace_size(p, 3); p->V, v_offset and v_total are not used
+ * beyond argument checks. */
+ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
+                             const int32_t* idx, const float* tlogit,
+                             float* lse_part, float* cross_part,
+                             void* ws, size_t ws_bytes, void* stream);
+ckl_status ckl_shard_combine(const ckl_problem* p, int32_t n_shards,
+                             const float* lse_parts, const float* cross_parts,
+                             const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                             float* loss, float* lse, float* row_loss,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel classes for the timing records below. */
 typedef enum {

@@ -60,6 +60,10 @@ def _prob(**kw):
     (dict(d=131072), B.CKL_ERR_UNSUPPORTED),
     (dict(T=4000001), B.CKL_ERR_UNSUPPORTED),
     (dict(teacher_form=2), B.CKL_ERR_INVALID_ARG),
+    (dict(v_offset=-1), B.CKL_ERR_INVALID_ARG),
+    (dict(v_offset=10, v_total=2050), B.CKL_ERR_INVALID_ARG),   # shard past the vocabulary end
+    (dict(v_total=1 << 31), B.CKL_ERR_UNSUPPORTED),
+    (dict(K=3000, V=2048, v_total=2048), B.CKL_ERR_INVALID_ARG),
     (dict(teacher_form=-1), B.CKL_ERR_INVALID_ARG),
     (dict(V=4000001), B.CKL_ERR_UNSUPPORTED),
 ])
@@ -72,9 +76,10 @@ def test_problem_validation(lib, kw, status):
 
 def test_workspace_query_and_plan(lib):
     p = _prob()
-    assert B.workspace_size(p, 0) > 0 and B.workspace_size(p, 1) > 0 and B.workspace_size(p, 2) > 0
+    for which in range(4):
+        assert B.workspace_size(p, which) > 0
     with pytest.raises(B.CklError):
-        B.workspace_size(p, 3)
+        B.workspace_size(p, 4)
     plan = B.backward_plan(p)
     assert plan["Tc"] % 128 == 0 and plan["Vc"] % 128 == 0  # fp32 tiles are 128 x 128
     assert plan["nT"] * plan["Tc"] >= 256 and plan["nV"] * plan["Vc"] >= 2048
@@ -163,3 +168,26 @@ def test_fused_plan_and_workspace(lib):
     assert c - b == pytest.approx(2 * (b - a), rel=1e-3)
     g2k, g4k = ws(32768, 2048), ws(32768, 4096)
     assert g4k - g2k == pytest.approx(2 * 2048 * (201088 + 128) * 2, rel=0.05)
+
+
+def test_shard_entry_points_reject_misuse(lib):
+    fake = 0x10000
+    shard = _prob(V=1000, v_offset=1000, v_total=2048)
+    # the whole-vocabulary entry points refuse a shard
+    st = lib.ckl_forward(ctypes.byref(shard), fake, fake, fake, fake, None, fake, fake, None, fake, 1 << 30, None)
+    assert st == B.CKL_ERR_UNSUPPORTED
+    st = lib.ckl_forward_backward(ctypes.byref(shard), fake, fake, fake, fake, None, None, fake, fake, None, fake,
+                                  fake, fake, 1 << 30, None)
+    assert st == B.CKL_ERR_UNSUPPORTED
+    # K may exceed the shard's rows as long as it fits the whole vocabulary
+    assert B.workspace_size(_prob(V=8, K=16, v_total=2048), 0) > 0
+    # shard forward: missing output, short workspace
+    st = lib.ckl_shard_forward(ctypes.byref(shard), fake, fake, fake, fake, None, fake, fake, 1 << 30, None)
+    assert st == B.CKL_ERR_INVALID_ARG
+    need = B.workspace_size(shard, 0)
+    st = lib.ckl_shard_forward(ctypes.byref(shard), fake, fake, fake, fake, fake, fake, fake, need - 1, None)
+    assert st == B.CKL_ERR_WORKSPACE
+    # combine: no shards
+    st = lib.ckl_shard_combine(ctypes.byref(shard), 0, fake, fake, fake, fake, None, fake, fake, None, fake, 1 << 30,
+                               None)
+    assert st == B.CKL_ERR_INVALID_ARG
