@@ -47,6 +47,10 @@ constexpr int64_t kMaxRows = 4000000;
 constexpr int64_t kCUs = 256;
 // dH split-k parts of the fused call: about this many dH tiles per chunk.
 constexpr int64_t kSplitTiles = 1024;
+// Fused call: G^T keeps the columns of this many consecutive row chunks, so
+// the dW update (an fp32 read-modify-write of all of dW) runs once per group
+// with k = kDwChunks * chunk rows instead of once per chunk.
+constexpr int64_t kDwChunks = 2;
 // The backward keeps one G block, stored as G and G^T, within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
 // the contraction of block i on a second stream measured no faster: both
@@ -292,7 +296,7 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
   w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
   w.G = take((size_t)q.Cs * (q.Vp + kLdPad) * q.esz);
-  w.Gt = take((size_t)q.Vp * (q.Cs + kLdPad) * q.esz);
+  w.Gt = take((size_t)q.Vp * (kDwChunks * q.Cs + kLdPad) * q.esz);
   w.mtab = take((size_t)q.groups * q.Cs * 4);
   w.dHp = take((size_t)q.Sh * q.Cs * q.d * 4);
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
@@ -534,7 +538,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   float* dHp = (float*)(b + w.dHp);
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
-  const int64_t ldG = q.Vp + kLdPad, ldGt = q.Cs + kLdPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
+  const int64_t ldG = q.Vp + kLdPad, ldGt = kDwChunks * q.Cs + kLdPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
 
   HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
@@ -561,6 +565,9 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     const int64_t tb0 = c * q.Cs;
     const int rows = (int)std::min(q.Cs, q.T - tb0);           // real rows of the chunk
     const int rows_p = (int)std::min(q.Cs, q.Tp - tb0);        // whole logit tiles
+    const int64_t slot = c % kDwChunks;                          // this chunk's columns of G^T
+    char* Gtc = Gt + slot * q.Cs * q.esz;
+    const bool dw_now = slot == kDwChunks - 1 || c == q.nS - 1;  // the group's last chunk
     const char* Hc = (const char*)H + tb0 * q.d * q.esz;
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
@@ -577,25 +584,27 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
             "fwd_rows");
     HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
                   [&] {
-                    return ckl::launch_gpass(q.in_bf16, G, ldG, Gt, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
+                    return ckl::launch_gpass(q.in_bf16, G, ldG, Gtc, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
                                              rows, rows_p, V, (int)q.Vp, st);
                   }),
             "gpass");
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,
                   [&] {
                     return ckl::launch_gfix(q.in_bf16, rows, K, V, idx_s + tb0 * K, p_s + tb0 * K, zg_s + tb0 * K,
-                                            srow + tb0, M + tb0, lse + tb0, G, ldG, Gt, ldGt, st);
+                                            srow + tb0, M + tb0, lse + tb0, G, ldG, Gtc, ldGt, st);
                   }),
             "gfix");
-    // dH rows of the chunk as Sh split-k partials (long k: scheduled first),
-    // dW (+)= G^T H_chunk
+    // dH rows of the chunk as Sh split-k partials (long k: scheduled first);
+    // at the group's last chunk also dW (+)= G^T H over the group's rows
     ckl::GemmArgs gdh{G, ldG, Wt, ldW, dHp, q.d, rows, d, (int)q.Vs, 0};
     gdh.batches = (int)q.Sh;
     gdh.kdim_last = (int)(q.Vp - (q.Sh - 1) * q.Vs);
     gdh.xb = q.Vs;
     gdh.yb = q.Vs;
     gdh.ob = q.Cs * q.d;
-    const ckl::GemmArgs gdw{Gt, ldGt, Ht + tb0 * q.esz, ldH, dWacc, q.d, V, d, rows_p, c > 0};
+    const int64_t g0 = c - slot;  // first chunk of the group
+    const ckl::GemmArgs gdw{Gt, ldGt, Ht + g0 * q.Cs * q.esz, ldH, dWacc, q.d, dw_now ? V : 0, d,
+                            (int)(slot * q.Cs + rows_p), g0 > 0};
     HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdh, gdw, st); }),
             "gemm dH parts + dW");
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,

@@ -184,3 +184,15 @@ def test_fused_logprob_teacher():
     say(f"case fused log-prob teacher cfg2 slice T={y.T}")
     got = run_gpu_fused(y, teacher_form=1)
     check_full(y, got, oracle_full(y, teacher_form=1), TOL["bf16"], 2e-3)
+
+
+def test_fused_odd_chunk_count():
+    # three 256-row chunks (the last ragged): the dW update of the last group
+    # covers one chunk only
+    import chunked_kl_loss_amd as ckl
+    x = inputs(1, T=700)
+    plan = ckl.fused_plan(ckl.make_problem(x.T, x.d, x.V, x.K, 200))
+    assert plan["chunks"] == 3
+    say(f"case fused odd chunk count T={x.T} plan={plan}")
+    got = run_gpu_fused(x, chunk=200, grad_loss=1.25)
+    check_full(x, got, oracle_full(x, grad_loss=1.25), TOL["bf16"], 2e-3)
