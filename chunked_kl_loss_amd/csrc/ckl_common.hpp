@@ -17,16 +17,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kIdxEnd = 0x7fffffff;  // sentinel past every vocabulary index
 
-// bf16 <-> f32.  Widening is exact; narrowing rounds to nearest, ties to even
-// (finite inputs only: the values rounded here are finite by construction).
+// bf16 <-> f32.  Widening is exact; narrowing rounds to nearest, ties to
+// even: the language conversion, which gfx950 executes as one
+// v_cvt_pk_bf16_f32 per pair of values.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2 v = {(bf16_t)lo, (bf16_t)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)f);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
