@@ -862,10 +862,11 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
 // ---------------------------------------------------------------- launchers --
 // bf16: 256 x 256 tiles on 64-wide k slices, 8 waves (2 per SIMD, so one
 // wave's loads, barriers and epilogue overlap the other's MFMAs).  The fused
-// logit kernels keep their epilogue state in the registers the plain dH / dW
-// contraction spends on double-buffered fragments.  fp32 (small problems):
+// logit kernels pipeline fragment reads per k16 substep, keeping for their
+// epilogue state the registers the plain dH / dW contraction spends on
+// fragments double-buffered per half stage.  fp32 (small problems):
 // 128 x 128 tiles, register-staged loads.
-using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 0>;
+using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
 using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
 using CfgBF16Gemm = Dma64Cfg<256, 256, 128, 64, 1>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;

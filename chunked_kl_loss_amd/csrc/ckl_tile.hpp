@@ -534,6 +534,11 @@ template <class C>
 struct Frags {
   bf16x8 a[2][C::MB], b[2][C::NB];
 };
+// fragments of one k16 substep
+template <class C>
+struct SubFrags {
+  bf16x8 a[C::MB], b[C::NB];
+};
 
 template <class C>
 __device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
@@ -732,7 +737,8 @@ __device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __re
 // PIPE = 0 drops the register double-buffering of the fragments (for kernels
 // whose epilogue state leaves no room for it): each stage is then read and
 // multiplied one k16 substep at a time, and the finished stage is refilled
-// right after the barrier that starts the next one.
+// right after the barrier that starts the next one.  PIPE = 2 pipelines at
+// substep granularity (two fragment sets of one substep each).
 //
 // BUF = 0 issues global_load_lds with per-lane 64-bit addresses (rows past the
 // end re-read row 0, chunks past kdim read a zero block) instead of buffer
@@ -899,7 +905,82 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
 
   const int nk = (kdim + C::BK - 1) / C::BK;
   const int n_full = kdim / C::BK;
-  if constexpr (!C::PIPE) {
+  if constexpr (C::PIPE == 2) {
+    // Substep pipeline: the fragments of k16 substep q + 1 are read under the
+    // MFMAs of substep q (two fragment sets of one substep each).  At the last
+    // substep of stage kt every wave has finished reading it: after the wait
+    // for slice kt + 1 and the barrier, stage kt is refilled with slice kt + 2.
+    using SF = SubFrags<C>;
+    auto sread = [&](int kt, int sub, SF& f, int w) {
+      const char* st = smem + (kt & 1) * C::STAGE_BYTES;
+      if (w < C::MB)
+        f.a[w] = *reinterpret_cast<const bf16x8*>(st + xwave + w * 32 * C::ROW_BYTES + roff[sub]);
+      else
+        f.b[w - C::MB] =
+            *reinterpret_cast<const bf16x8*>(st + ywave + (w - C::MB) * 32 * C::ROW_BYTES + roff[sub]);
+    };
+    constexpr int kM = C::MB * C::NB, kR = C::MB + C::NB;
+    // one substep: MFMAs with `cur`; reads of (rkt, rsub) into `nxt`, and at
+    // the last substep the refill of slice kt + 2 first
+    auto substep = [&](int kt, const SF& cur, SF& nxt, int rkt, int rsub, bool rd, bool last, bool refill,
+                       bool whole) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm0();
+      if (last && rd) {
+        wait_vmcnt<0>();
+        phase_barrier();
+      }
+      constexpr int kOps = kR + kDma;
+#pragma unroll
+      for (int j = 0; j < kM; ++j) {
+        tile.acc[j / C::NB][j % C::NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            cur.a[j / C::NB], cur.b[j % C::NB], tile.acc[j / C::NB][j % C::NB], 0, 0, 0);
+        if (last) {
+#pragma unroll
+          for (int q = j * kOps / kM; q < (j + 1) * kOps / kM; ++q) {
+            if (q < kDma) {
+              if (refill) dma(kt + 2, q, whole);
+            } else if (rd) {
+              sread(rkt, rsub, nxt, q - kDma);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = j * kR / kM; q < (j + 1) * kR / kM; ++q) sread(rkt, rsub, nxt, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
+      if (nk > 1) {
+#pragma unroll
+        for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
+        wait_vmcnt<kDma>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      phase_barrier();
+      SF fa, fb;
+#pragma unroll
+      for (int w = 0; w < kR; ++w) sread(0, 0, fa, w);
+      int kt = 0;
+      for (; kt + 2 < n_full; ++kt) {  // steady state: the refilled slice is whole
+        substep(kt, fa, fb, kt, 1, true, false, false, true);
+        substep(kt, fb, fa, kt, 2, true, false, false, true);
+        substep(kt, fa, fb, kt, 3, true, false, false, true);
+        substep(kt, fb, fa, kt + 1, 0, true, true, true, true);
+      }
+      for (; kt < nk; ++kt) {
+        const bool next = kt + 1 < nk;
+        substep(kt, fa, fb, kt, 1, true, false, false, true);
+        substep(kt, fb, fa, kt, 2, true, false, false, true);
+        substep(kt, fa, fb, kt, 3, true, false, false, true);
+        substep(kt, fb, fa, kt + 1, 0, next, true, kt + 2 < nk, kt + 2 < n_full);
+      }
+    }
+  } else if constexpr (!C::PIPE) {
     if (nk > 0) {
 #pragma unroll
       for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
