@@ -237,9 +237,22 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   }
 
   typename C::TileT tile;
+  // With the substep loop, the next tile's first two slices are issued right
+  // after a tile's k loop, so that their latency overlaps this tile's epilogue
+  // (registers and global memory only; the LDS stages are untouched).
+  constexpr bool kAhead = PrefetchOK<C>::value;
+  const TIn* Ht0 = H + (int64_t)t0 * d;
+  if constexpr (kAhead)
+    if (vt0 < vt1) tile_k64_prologue<C>(W + (int64_t)vt0 * C::BM * d, d, V - vt0 * C::BM, Ht0, d, T - t0, d, smem);
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vt * C::BM;
-    run_mma(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    if constexpr (kAhead) {
+      run_mma<C, true>(tile, W + (int64_t)v0 * d, d, V - v0, Ht0, d, T - t0, d, smem);
+      if (vt + 1 < vt1)
+        tile_k64_prologue<C>(W + (int64_t)(v0 + C::BM) * d, d, V - v0 - C::BM, Ht0, d, T - t0, d, smem);
+    } else {
+      run_mma(tile, W + (int64_t)v0 * d, d, V - v0, Ht0, d, T - t0, d, smem);
+    }
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
 #pragma unroll

@@ -766,15 +766,97 @@ struct Dma64Cfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
+// Operand loader of the 64-wide loop.  With BUF: buffer_load ... lds through
+// one buffer resource per operand, based at the tile's first row and bounded
+// by its valid rows, so rows past xrows / yrows read as zero without a clamp;
+// per-lane byte offsets stay fixed and the k slice advances in the scalar
+// offset.  Without BUF: global_load_lds with element offsets (rows past the
+// end re-read row 0).  Lane -> (row within its 8-row group, slot); the rows
+// of load i are (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for
+// every i since NWAVES is even.
+template <class C>
+struct K64Loader {
+  const bf16_t* X;
+  const bf16_t* Y;
+  __amdgpu_buffer_rsrc_t rx, ry;  // (unused, and dropped by the compiler, when BUF = 0)
+  uint32_t off[C::LOADS_PER_STAGE];
+  int wave, lchunk, kdim;
+  __device__ __forceinline__ K64Loader(const bf16_t* X_, int64_t ldx, int xrows, const bf16_t* Y_, int64_t ldy,
+                                       int yrows, int kdim_)
+      : X(X_),
+        Y(Y_),
+        rx(make_rsrc(X_, (uint32_t)(min(xrows, C::BM) * ldx * 2))),
+        ry(make_rsrc(Y_, (uint32_t)(min(yrows, C::BN) * ldy * 2))),
+        kdim(kdim_) {
+    const int lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    const int lrow = lane >> 3;
+    lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
+#pragma unroll
+    for (int i = 0; i < C::X_LOADS; ++i) {
+      const int row = (wave + i * C::NWAVES) * 8 + lrow;
+      off[i] = C::BUF ? (uint32_t)(row * ldx * 2 + lchunk * 16) : (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C::Y_LOADS; ++i) {
+      const int row = (wave + i * C::NWAVES) * 8 + lrow;
+      off[C::X_LOADS + i] =
+          C::BUF ? (uint32_t)(row * ldy * 2 + lchunk * 16) : (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
+    }
+  }
+  __device__ __forceinline__ char* lds_at(char* smem, int kt, int i) const {
+    char* st = smem + (kt & 1) * C::STAGE_BYTES;
+    return i < C::X_LOADS ? st + (wave + i * C::NWAVES) * 1024
+                          : st + C::X_BYTES + (wave + (i - C::X_LOADS) * C::NWAVES) * 1024;
+  }
+  // load i of slice kt; `whole`: the slice lies inside [0, kdim).  Chunks past
+  // kdim load zeros: an offset past every record (buffer loads) or the zero
+  // block.
+  __device__ __forceinline__ void dma(char* smem, int kt, int i, bool whole) const {
+    const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
+    if constexpr (C::BUF) {
+      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? off[i] : kOutOfRange, (uint32_t)(kt * C::BK * 2),
+                  lds_at(smem, kt, i));
+    } else {
+      const bf16_t* src = (i < C::X_LOADS ? X : Y) + kt * C::BK + off[i];
+      lds_dma16(in ? (const void*)src : (const void*)kZeroChunk, lds_at(smem, kt, i));
+    }
+  }
+  // the first two slices (the loop's prologue)
+  __device__ __forceinline__ void prologue(char* smem) const {
+    const int nk = (kdim + C::BK - 1) / C::BK, n_full = kdim / C::BK;
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS_PER_STAGE; ++i) dma(smem, 0, i, n_full > 0);
+    }
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS_PER_STAGE; ++i) dma(smem, 1, i, n_full > 1);
+    }
+  }
+};
+
+// Issue the first two slices of a tile whose loop runs later with PRE = true
+// (the caller may do other work meanwhile, without touching the LDS stages).
+template <class C>
+__device__ __forceinline__ void tile_k64_prologue(const bf16_t* __restrict__ X, int64_t ldx, int xrows,
+                                                  const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
+                                                  char* smem) {
+  K64Loader<C>(X, ldx, xrows, Y, ldy, yrows, kdim).prologue(smem);
+}
+
 // Same contract as tile_mma_dma (kdim a multiple of 8; k past kdim reads as
 // zero; rows past xrows / yrows give garbage outputs to discard; ends with a
 // barrier), except that offsets are in bytes: BM * ldx * 2 and BN * ldy * 2
-// must stay below 2^31.
-template <class C>
+// must stay below 2^31.  PRE (PIPE = 2 only): the prologue was issued by
+// tile_k64_prologue with the same arguments; the loop starts by waiting for
+// every outstanding vector memory operation (stores count on this GPU).
+template <class C, bool PRE = false>
 __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
                                              const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
                                              char* smem) {
   static_assert(C::BK == 64 && C::NSTAGE == 2, "two 64-wide stages");
+  static_assert(!PRE || C::PIPE == 2, "prologue issued ahead only for the substep pipeline");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -788,54 +870,10 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
 
-  // Loader: buffer_load ... lds through one buffer resource per operand,
-  // based at the tile's first row and bounded by its valid rows, so rows past
-  // xrows / yrows read as zero without a clamp.  Lane -> (row within its 8-row
-  // group, slot); the rows of load i are (wave + i NWAVES) 8 + lrow, whose
-  // (r >> 1) & 7 is the same for every i since NWAVES is even.  The per-lane
-  // byte offsets stay fixed; the k slice advances in the scalar offset.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
-  auto lds_at = [&](int kt, int i) {
-    char* st = smem + (kt & 1) * C::STAGE_BYTES;
-    return i < C::X_LOADS ? st + (wave + i * C::NWAVES) * 1024
-                          : st + C::X_BYTES + (wave + (i - C::X_LOADS) * C::NWAVES) * 1024;
-  };
-  uint32_t off[C::LOADS_PER_STAGE];
-  // (unused, and dropped by the compiler, when BUF = 0)
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(min(xrows, C::BM) * ldx * 2));
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y, (uint32_t)(min(yrows, C::BN) * ldy * 2));
-  if constexpr (C::BUF) {
-#pragma unroll
-    for (int i = 0; i < C::X_LOADS; ++i)
-      off[i] = (uint32_t)(((wave + i * C::NWAVES) * 8 + lrow) * ldx * 2 + lchunk * 16);
-#pragma unroll
-    for (int i = 0; i < C::Y_LOADS; ++i)
-      off[C::X_LOADS + i] = (uint32_t)(((wave + i * C::NWAVES) * 8 + lrow) * ldy * 2 + lchunk * 16);
-  } else {  // element offsets; rows past the end re-read row 0
-#pragma unroll
-    for (int i = 0; i < C::X_LOADS; ++i) {
-      const int row = (wave + i * C::NWAVES) * 8 + lrow;
-      off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < C::Y_LOADS; ++i) {
-      const int row = (wave + i * C::NWAVES) * 8 + lrow;
-      off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-    }
-  }
-  // load i of slice kt; `whole`: the slice lies inside [0, kdim).  Chunks past
-  // kdim load zeros: an offset past every record (buffer loads) or the zero
-  // block.
-  auto dma = [&](int kt, int i, bool whole) {
-    const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
-    if constexpr (C::BUF) {
-      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? off[i] : kOutOfRange, (uint32_t)(kt * C::BK * 2), lds_at(kt, i));
-    } else {
-      const bf16_t* src = (i < C::X_LOADS ? X : Y) + kt * C::BK + off[i];
-      lds_dma16(in ? (const void*)src : (const void*)kZeroChunk, lds_at(kt, i));
-    }
-  };
+  const K64Loader<C> ld(X, ldx, xrows, Y, ldy, yrows, kdim);
+  const int lchunk = ld.lchunk;
+  (void)lchunk;
+  auto dma = [&](int kt, int i, bool whole) { ld.dma(smem, kt, i, whole); };
 
   // Reader: lane reads row (lane & 31) + 32 block of its wave's rows, chunk
   // 2 sub + (lane >> 5) for k16 substep sub of the stage.
@@ -952,14 +990,18 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
       }
     };
     if (nk > 0) {
-#pragma unroll
-      for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
-      if (nk > 1) {
-#pragma unroll
-        for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
-        wait_vmcnt<kDma>();
-      } else {
+      if constexpr (PRE) {
         wait_vmcnt<0>();
+      } else {
+#pragma unroll
+        for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
+        if (nk > 1) {
+#pragma unroll
+          for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
+          wait_vmcnt<kDma>();
+        } else {
+          wait_vmcnt<0>();
+        }
       }
       phase_barrier();
       SF fa, fb;
@@ -1075,16 +1117,22 @@ __device__ __forceinline__ void grouped_mn(int L, int tiles_m, int tiles_n, int 
   n = r / rows;
 }
 
+// Configurations whose loop can take a prologue issued ahead (tile_k64_prologue).
+template <class C>
+struct PrefetchOK : std::false_type {};
+template <int BM, int BN, int WM, int WN, int BUF>
+struct PrefetchOK<Dma64Cfg<BM, BN, WM, WN, 2, BUF>> : std::true_type {};
+
 // One entry point for both main loops.
 template <class C>
 __device__ __forceinline__ void run_mma(Tile<C>& t, const typename C::TIn* X, int64_t ldx, int xrows,
                                         const typename C::TIn* Y, int64_t ldy, int yrows, int kdim, char* smem) {
   tile_mma<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, reinterpret_cast<typename C::TIn*>(smem));
 }
-template <class C>
+template <class C, bool PRE = false>
 __device__ __forceinline__ void run_mma(DmaTile<C>& t, const bf16_t* X, int64_t ldx, int xrows, const bf16_t* Y,
                                         int64_t ldy, int yrows, int kdim, char* smem) {
-  if constexpr (C::BK == 64) tile_mma_k64<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
+  if constexpr (C::BK == 64) tile_mma_k64<C, PRE>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
   else if constexpr (C::NWAVES == 4) tile_mma_sp<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
   else tile_mma_dma<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
 }
