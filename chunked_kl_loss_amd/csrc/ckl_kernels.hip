@@ -837,19 +837,39 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
           }
       }
       __syncthreads();
-      for (int i = threadIdx.x; i < HALF * (C::BN / 4); i += C::NTHREADS) {
+      // Every thread's old values are loaded before any of its stores: loads
+      // and stores of one output array would otherwise stay in program order,
+      // one round trip per 16 bytes.
+      constexpr int PER = HALF * (C::BN / 4) / C::NTHREADS;
+      constexpr int BATCH = PER < 8 ? PER : 8;  // float4 loads in flight (registers: the other half's acc is live)
+      static_assert(HALF * (C::BN / 4) % C::NTHREADS == 0 && PER % BATCH == 0, "whole float4 batches");
+#pragma unroll
+      for (int j0 = 0; j0 < PER; j0 += BATCH) {
+      f32x4 old[BATCH];
+#pragma unroll
+      for (int jj = 0; jj < BATCH; ++jj) {
+        const int i = threadIdx.x + (j0 + jj) * C::NTHREADS;
+        const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
+        const int m = m0 + half * HALF + ml, n = n0 + c4;
+        old[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (beta && vec_ok && m < M && n + 4 <= N)
+          old[jj] = *reinterpret_cast<const f32x4*>(out + (int64_t)m * ldo + n);
+      }
+#pragma unroll
+      for (int jj = 0; jj < BATCH; ++jj) {
+        const int j = jj;
+        const int i = threadIdx.x + (j0 + jj) * C::NTHREADS;
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
         const int m = m0 + half * HALF + ml, n = n0 + c4;
         if (m >= M || n >= N) continue;
         const float* sv = st + ml * C::BN + c4;
         float* o = out + (int64_t)m * ldo + n;
         if (vec_ok && n + 4 <= N) {
-          f32x4 v = *reinterpret_cast<const f32x4*>(sv);
-          if (beta) v += *reinterpret_cast<const f32x4*>(o);
-          *reinterpret_cast<f32x4*>(o) = v;
+          *reinterpret_cast<f32x4*>(o) = *reinterpret_cast<const f32x4*>(sv) + old[j];
         } else {
           for (int e = 0; e < 4 && n + e < N; ++e) o[e] = beta ? o[e] + sv[e] : sv[e];
         }
+      }
       }
       __syncthreads();
     }
