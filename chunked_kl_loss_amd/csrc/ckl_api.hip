@@ -45,12 +45,15 @@ constexpr int64_t kMaxRows = 4000000;
 // Compute units of an MI355X; the logit and contraction kernels fit one
 // workgroup per CU (128 KiB of LDS each), so kCUs workgroups make one wave.
 constexpr int64_t kCUs = 256;
-// dH split-k parts of the fused call: about this many dH tiles per chunk.
-constexpr int64_t kSplitTiles = 1024;
+// dH split-k parts of the fused call: at most this many, and the fp32 store
+// of one part's tile costs about as long as this many k columns of its
+// main loop (a 256 x 256 fp32 tile at one CU's share of HBM bandwidth).
+constexpr int64_t kMaxSplit = 64;
+constexpr int64_t kEpilogueK = 512;
 // Fused call: G^T keeps the columns of this many consecutive row chunks, so
 // the dW update (an fp32 read-modify-write of all of dW) runs once per group
 // with k = kDwChunks * chunk rows instead of once per chunk.
-constexpr int64_t kDwChunks = 2;
+constexpr int64_t kDwChunks = 4;
 // The backward keeps one G block, stored as G and G^T, within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
 // the contraction of block i on a second stream measured no faster: both
@@ -222,11 +225,24 @@ Plan make_plan(const ckl_problem* p) {
   q.Cs = std::min(round_up(p->chunk, 256), round_up(q.Tp, 256));
   q.nS = ceil_div(q.Tp, q.Cs);
   pick_splits(q.Cs / q.BN, q.Vp / q.BM, &q.c_splits, &q.c_tps);
+  // dH split-k parts: the count whose tiles finish in the fewest k-steps when
+  // dealt to kCUs workgroups in rounds (whole rounds: a launch that holds only
+  // dH tiles ends with its slowest round), each part also paying its epilogue.
   const int64_t gtile = ckl::gemm_tile(q.in_bf16);
   const int64_t dh_tiles = ceil_div(q.Cs, gtile) * ceil_div(q.d, gtile);
-  const int64_t sh = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kSplitTiles, dh_tiles), q.Vp / 256));
-  q.Vs = round_up(ceil_div(q.Vp, sh), 256);
-  q.Sh = ceil_div(q.Vp, q.Vs);
+  const int64_t sh_max = std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, q.Vp / 256));
+  int64_t best_cost = -1;
+  for (int64_t sh = 1; sh <= sh_max; ++sh) {
+    const int64_t vs = round_up(ceil_div(q.Vp, sh), 256);
+    const int64_t parts = ceil_div(q.Vp, vs);
+    if (parts != sh) continue;  // the same split as a smaller count
+    const int64_t cost = ceil_div(dh_tiles * parts, kCUs) * (vs + kEpilogueK);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      q.Vs = vs;
+      q.Sh = parts;
+    }
+  }
   q.groups = (q.Vp / q.BM) * ckl::lse_groups_per_tile(q.in_bf16);
   return q;
 }

@@ -195,49 +195,11 @@ __device__ __forceinline__ void tile_mma(Tile<C>& tile, const typename C::TIn* _
 }
 
 // ---------------------------------------------------------------------------
-// bf16 main loop with direct global->LDS loads (global_load_lds_dwordx4).
-//
-// NSTAGE LDS stages of BK = 32 k-columns each hold the X tile [BM][32] and the
-// Y tile [BN][32]; a row is 64 bytes = four 16-byte chunks.  The chunk with k
-// offset 8c of row r sits in slot c ^ ((r >> 2) & 3), so that the sixteen
-// lanes of one ds_read_b128 quarter-wave (sixteen consecutive rows, one
-// chunk) hit sixteen distinct 16-byte bank groups.
-//
-// A wave's global_load_lds writes 64 lanes x 16 bytes contiguously at the
-// (wave-uniform) LDS address, i.e. 16 rows x 4 slots; each lane therefore
-// fetches the global chunk that belongs in its slot.  Lanes outside the valid
-// rows / k range fetch a 16-byte zero block instead.
-//
-// Pipeline: stages kt+1 .. kt+NSTAGE-1 are in flight while stage kt is
-// multiplied.  Each iteration waits (vmcnt) for this thread's own loads of
-// stage kt, then an s_barrier makes every thread's loads visible and frees
-// the stage read in the previous iteration, which is refilled at once.
+// Direct global->LDS load helpers of the bf16 main loop.
 // ---------------------------------------------------------------------------
+// A 16-byte zero block: the per-lane address of a load whose k range lies
+// past the end of the operand.
 __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
-
-template <class C>
-struct DmaTile;
-
-template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_>
-struct DmaCfg {
-  using TIn = bf16_t;
-  using TileT = DmaTile<DmaCfg>;
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int NWAVES = WAVES_M * WAVES_N;
-  static constexpr int NTHREADS = 64 * NWAVES;
-  static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int BK = 32;
-  static constexpr int ROW_BYTES = 64;
-  static constexpr int X_BYTES = BM * ROW_BYTES, Y_BYTES = BN * ROW_BYTES;
-  static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-  // one wave-instruction fills 16 rows; loads per thread per stage
-  static constexpr int X_LOADS = BM / 16 / NWAVES, Y_LOADS = BN / 16 / NWAVES;
-  static constexpr int LOADS_PER_STAGE = X_LOADS + Y_LOADS;
-  static_assert(BM % (16 * NWAVES) == 0 && BN % (16 * NWAVES) == 0, "row groups per wave");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-};
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -264,134 +226,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// Accumulators of one wave's MB x NB blocks of 32 x 32 outputs.
 template <class C>
 struct DmaTile {
   f32x16 acc[C::MB][C::NB];
 };
 
-// Computes the BM x BN tile over k in [0, kdim) (kdim a multiple of 8).  k
-// past kdim reads as zero; rows past xrows / yrows read arbitrary valid data,
-// so output rows >= xrows and columns >= yrows hold garbage that callers must
-// discard (select, never multiply).  Row offsets row * ld + k must fit in 32
-// bits.  Ends with a barrier after which the LDS may be reused.
-template <class C>
-__device__ __forceinline__ void tile_mma_dma(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
-                                             const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
-                                             char* smem) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wave_m = wave / C::WAVES_N;
-  const int wave_n = wave % C::WAVES_N;
-
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
-
-  // Loader: lane -> (row within its 16-row group, slot); the chunk in that
-  // slot is c = slot ^ ((row >> 2) & 3).  Rows past the valid count re-read
-  // row 0 (they only feed output rows / columns the callers discard); k past
-  // kdim reads the zero block, so the valid outputs stay exact.
-  const int lrow = lane >> 2;
-  const int lslot = lane & 3;
-  const int lchunk = lslot ^ ((lrow >> 2) & 3);
-  uint32_t xoff[C::X_LOADS], yoff[C::Y_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::X_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    xoff[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < C::Y_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    yoff[i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-  }
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % C::NSTAGE) * C::STAGE_BYTES;
-    const int k0 = kt * C::BK;
-    const bf16_t* xk = X + k0;
-    const bf16_t* yk = Y + k0;
-    if (k0 + C::BK <= kdim) {  // whole slice in range (wave-uniform)
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) lds_dma16(xk + xoff[i], st + (wave + i * C::NWAVES) * 1024);
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) lds_dma16(yk + yoff[i], st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-    } else {  // final partial slice: chunks past kdim read the zero block
-      const bool kok = k0 + lchunk * 8 < kdim;
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) {
-        const void* g = kok ? (const void*)(xk + xoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + (wave + i * C::NWAVES) * 1024);
-      }
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) {
-        const void* g = kok ? (const void*)(yk + yoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-      }
-    }
-  };
-
-  // Reader offsets: lane reads row (lane & 31) + 32 mb of its wave's rows,
-  // chunk 2 s + (lane >> 5); the swizzle only depends on (lane & 31) >> 2.
-  const int rrow = lane & 31;
-  const int rsw = (rrow >> 2) & 3;
-  int roff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) roff[s] = rrow * C::ROW_BYTES + (((2 * s + (lane >> 5)) ^ rsw) * 16);
-  const int xwave = wave_m * C::WM * C::ROW_BYTES;
-  const int ywave = C::X_BYTES + wave_n * C::WN * C::ROW_BYTES;
-
-  const int nk = (kdim + C::BK - 1) / C::BK;
-#pragma unroll
-  for (int p = 0; p < C::NSTAGE - 1; ++p)
-    if (p < nk) issue(p);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // this thread's loads of stage kt are complete once at most the loads of
-    // the later stages already issued remain outstanding
-    const int later = min(C::NSTAGE - 2, nk - 1 - kt);
-    if (later >= 2) wait_vmcnt<2 * C::LOADS_PER_STAGE>();
-    else if (later == 1) wait_vmcnt<C::LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + C::NSTAGE - 1 < nk) issue(kt + C::NSTAGE - 1);
-    const char* st = smem + (kt % C::NSTAGE) * C::STAGE_BYTES;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 a[C::MB], b[C::NB];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        a[mb] = *reinterpret_cast<const bf16x8*>(st + xwave + mb * 32 * C::ROW_BYTES + roff[s]);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-        b[nb] = *reinterpret_cast<const bf16x8*>(st + ywave + nb * 32 * C::ROW_BYTES + roff[s]);
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-          tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], tile.acc[mb][nb], 0, 0, 0);
-    }
-  }
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// Ping-pong variant of the same main loop.  Waves w and w + 4 share a SIMD;
-// they form group 0 (waves 0-3) and group 1 (waves 4-7).  Every k-step has a
-// memory phase (LDS fragment reads for the step) and a compute phase (its 16
-// MFMAs), and the groups run one phase apart, separated by workgroup
-// barriers: while one wave of a SIMD feeds the matrix core, the other reads
-// LDS, so the MFMA pipe never drains at a barrier.  Group 1 starts one
-// barrier late and group 0 ends with one extra barrier, so both groups
-// execute the same number of barriers.
-//
-// Stage s (of NSTAGE LDS stages) is refilled in global phase 2(s-NSTAGE)+2,
-// right after both groups finished reading it, and is waited for (vmcnt, per
-// thread) before the barrier that ends global phase 2s-1.
-// ---------------------------------------------------------------------------
+// Workgroup barrier the compiler may not move work across.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
@@ -399,327 +240,23 @@ __device__ __forceinline__ void phase_barrier() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <class C>
-__device__ __forceinline__ void tile_mma_pp(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
-                                            const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
-                                            char* smem) {
-  static_assert(C::NWAVES == 8, "ping-pong pairs the two waves of each SIMD");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int grp = wave >> 2;
-  const int wave_m = wave / C::WAVES_N;
-  const int wave_n = wave % C::WAVES_N;
-
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
-
-  const int lrow = lane >> 2;
-  const int lslot = lane & 3;
-  const int lchunk = lslot ^ ((lrow >> 2) & 3);
-  uint32_t xoff[C::X_LOADS], yoff[C::Y_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::X_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    xoff[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < C::Y_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    yoff[i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-  }
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % C::NSTAGE) * C::STAGE_BYTES;
-    const int k0 = kt * C::BK;
-    const bf16_t* xk = X + k0;
-    const bf16_t* yk = Y + k0;
-    if (k0 + C::BK <= kdim) {
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) lds_dma16(xk + xoff[i], st + (wave + i * C::NWAVES) * 1024);
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) lds_dma16(yk + yoff[i], st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-    } else {
-      const bool kok = k0 + lchunk * 8 < kdim;
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) {
-        const void* g = kok ? (const void*)(xk + xoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + (wave + i * C::NWAVES) * 1024);
-      }
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) {
-        const void* g = kok ? (const void*)(yk + yoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-      }
-    }
-  };
-  const int nk = (kdim + C::BK - 1) / C::BK;
-  // Wait until this thread's loads of stage s are complete: the loads of at
-  // most min(NSTAGE - 2, nk - 1 - s) later stages may still be in flight.
-  auto wait_stage = [&](int s) {
-    const int later = min(C::NSTAGE - 2, nk - 1 - s);
-    if (later >= 3) wait_vmcnt<3 * C::LOADS_PER_STAGE>();
-    else if (later == 2) wait_vmcnt<2 * C::LOADS_PER_STAGE>();
-    else if (later == 1) wait_vmcnt<C::LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
-  };
-  static_assert(C::NSTAGE <= 5, "wait_stage covers up to three later stages");
-
-  const int rrow = lane & 31;
-  const int rsw = (rrow >> 2) & 3;
-  int roff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) roff[s] = rrow * C::ROW_BYTES + (((2 * s + (lane >> 5)) ^ rsw) * 16);
-  const int xwave = wave_m * C::WM * C::ROW_BYTES;
-  const int ywave = C::X_BYTES + wave_n * C::WN * C::ROW_BYTES;
-
-#pragma unroll
-  for (int p = 0; p < C::NSTAGE; ++p)
-    if (p < nk) issue(p);
-  wait_stage(0);
-  phase_barrier();
-  if (grp == 1) phase_barrier();
-
-  for (int j = 0; j < nk; ++j) {
-    // memory phase of step j
-    const char* st = smem + (j % C::NSTAGE) * C::STAGE_BYTES;
-    bf16x8 a[2][C::MB], b[2][C::NB];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        a[s][mb] = *reinterpret_cast<const bf16x8*>(st + xwave + mb * 32 * C::ROW_BYTES + roff[s]);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-        b[s][nb] = *reinterpret_cast<const bf16x8*>(st + ywave + nb * 32 * C::ROW_BYTES + roff[s]);
-    }
-    if (grp == 0) {
-      if (j >= 1 && j - 1 + C::NSTAGE < nk) issue(j - 1 + C::NSTAGE);
-    } else {
-      if (j + 1 < nk) wait_stage(j + 1);
-    }
-    wait_lgkm0();
-    phase_barrier();
-    // compute phase of step j
-    if (grp == 1 && j + C::NSTAGE < nk) issue(j + C::NSTAGE);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-          tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][mb], b[s][nb], tile.acc[mb][nb], 0, 0, 0);
-    if (grp == 0 && j + 1 < nk) wait_stage(j + 1);
-    phase_barrier();
-  }
-  if (grp == 0) phase_barrier();
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// Software-pipelined variant for one wave per SIMD (4 waves, 128 x 128 wave
-// tiles, accumulators in AGPRs).  Iteration k:
-//   wait for this thread's loads of stage k+1; barrier (stage k+1 visible to
-//   all, every wave done reading stage k-1); refill stage k-1's buffer with
-//   stage k+NSTAGE-1; issue the 16 LDS fragment reads of stage k+1 into the
-//   spare register set; then the 32 MFMAs of stage k from the other set.
-// The LDS latency of step k+1 hides under the MFMAs of step k, and the MFMA
-// pipe only pauses for the barrier.  Two register sets alternate through a
-// two-way unrolled loop, so nothing is copied.
-// ---------------------------------------------------------------------------
+// MFMA operand fragments read from LDS: two k16 substeps (Frags) or one
+// (SubFrags).
 template <class C>
 struct Frags {
   bf16x8 a[2][C::MB], b[2][C::NB];
 };
-// fragments of one k16 substep
 template <class C>
 struct SubFrags {
   bf16x8 a[C::MB], b[C::NB];
 };
-
-template <class C>
-__device__ __forceinline__ void tile_mma_sp(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
-                                            const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
-                                            char* smem) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wave_m = wave / C::WAVES_N;
-  const int wave_n = wave % C::WAVES_N;
-
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
-
-  const int lrow = lane >> 2;
-  const int lslot = lane & 3;
-  const int lchunk = lslot ^ ((lrow >> 2) & 3);
-  uint32_t xoff[C::X_LOADS], yoff[C::Y_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::X_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    xoff[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < C::Y_LOADS; ++i) {
-    const int row = (wave + i * C::NWAVES) * 16 + lrow;
-    yoff[i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-  }
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % C::NSTAGE) * C::STAGE_BYTES;
-    const int k0 = kt * C::BK;
-    const bf16_t* xk = X + k0;
-    const bf16_t* yk = Y + k0;
-    if (k0 + C::BK <= kdim) {
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) lds_dma16(xk + xoff[i], st + (wave + i * C::NWAVES) * 1024);
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) lds_dma16(yk + yoff[i], st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-    } else {
-      const bool kok = k0 + lchunk * 8 < kdim;
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) {
-        const void* g = kok ? (const void*)(xk + xoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + (wave + i * C::NWAVES) * 1024);
-      }
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) {
-        const void* g = kok ? (const void*)(yk + yoff[i]) : (const void*)kZeroChunk;
-        lds_dma16(g, st + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-      }
-    }
-  };
-  const int nk = (kdim + C::BK - 1) / C::BK;
-  // this thread's loads of stage s are complete once at most the later stages
-  // issued so far (s+1 .. s+NSTAGE-3 when waiting inside the loop) remain
-  auto wait_stage = [&](int s, int issued_last) {
-    const int later = min(issued_last, nk - 1) - s;
-    if (later >= 3) wait_vmcnt<3 * C::LOADS_PER_STAGE>();
-    else if (later == 2) wait_vmcnt<2 * C::LOADS_PER_STAGE>();
-    else if (later == 1) wait_vmcnt<C::LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
-  };
-  static_assert(C::NSTAGE >= 3 && C::NSTAGE <= 6, "stage count");
-  static_assert(3 * C::LOADS_PER_STAGE < 64, "vmcnt range");
-
-  const int rrow = lane & 31;
-  const int rsw = (rrow >> 2) & 3;
-  int roff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) roff[s] = rrow * C::ROW_BYTES + (((2 * s + (lane >> 5)) ^ rsw) * 16);
-  const int xwave = wave_m * C::WM * C::ROW_BYTES;
-  const int ywave = C::X_BYTES + wave_n * C::WN * C::ROW_BYTES;
-  auto read = [&](int kt, Frags<C>& f) {
-    const char* st = smem + (kt % C::NSTAGE) * C::STAGE_BYTES;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        f.a[s][mb] = *reinterpret_cast<const bf16x8*>(st + xwave + mb * 32 * C::ROW_BYTES + roff[s]);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-        f.b[s][nb] = *reinterpret_cast<const bf16x8*>(st + ywave + nb * 32 * C::ROW_BYTES + roff[s]);
-    }
-  };
-  auto mma = [&](const Frags<C>& f) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-          tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][mb], f.b[s][nb], tile.acc[mb][nb], 0, 0, 0);
-  };
-  // one pipelined step: stage kt is in `cur`; fetch stage kt+1 into `nxt`
-  auto step = [&](int kt, const Frags<C>& cur, Frags<C>& nxt) {
-    // `cur` was read a whole step ago: draining the LDS counter here is free,
-    // and leaves only the reads into `nxt` in flight during the MFMAs (the
-    // 4-bit LDS counter could not single out 16 older reads otherwise).
-    wait_lgkm0();
-    if (kt + 1 < nk) {
-      wait_stage(kt + 1, kt + C::NSTAGE - 2);
-      phase_barrier();
-      if (kt + C::NSTAGE - 1 < nk) issue(kt + C::NSTAGE - 1);
-      read(kt + 1, nxt);
-    }
-    mma(cur);
-  };
-  // The same step when every slice involved is whole and in range, in one
-  // fixed order: MFMA j of the current slice is followed by the j-th DMA of
-  // the refill (issued first, to give it the most time) and then by the LDS
-  // fragment reads of the next slice, one per MFMA.  Scheduling barriers pin
-  // the order (the scheduler would otherwise bunch the DMAs, stalling the
-  // only wave of the SIMD on the address queue).
-  const int fx = wave_m * C::WM, fy = wave_n * C::WN;
-  auto step_full = [&](int kt, const Frags<C>& cur, Frags<C>& nxt) {
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkm0();
-    wait_vmcnt<(C::NSTAGE - 3) * C::LOADS_PER_STAGE>();
-    phase_barrier();
-    char* dst = smem + ((kt + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE_BYTES;
-    const int k0 = (kt + C::NSTAGE - 1) * C::BK;
-    const char* src = smem + ((kt + 1) % C::NSTAGE) * C::STAGE_BYTES;
-    constexpr int kMfma = 2 * C::MB * C::NB;
-    constexpr int kReads = 2 * (C::MB + C::NB);
-    static_assert(C::LOADS_PER_STAGE + kReads <= kMfma, "one memory op per MFMA");
-#pragma unroll
-    for (int j = 0; j < kMfma; ++j) {
-      {
-        const int s = j / (C::MB * C::NB), mb = (j / C::NB) % C::MB, nb = j % C::NB;
-        tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[s][mb], cur.b[s][nb], tile.acc[mb][nb], 0, 0, 0);
-      }
-      if (j < C::X_LOADS) {
-        lds_dma16(X + k0 + xoff[j], dst + (wave + j * C::NWAVES) * 1024);
-      } else if (j < C::LOADS_PER_STAGE) {
-        const int i = j - C::X_LOADS;
-        lds_dma16(Y + k0 + yoff[i], dst + C::X_BYTES + (wave + i * C::NWAVES) * 1024);
-      } else if (j < C::LOADS_PER_STAGE + kReads) {
-        const int q = j - C::LOADS_PER_STAGE;
-        const int s = q / (C::MB + C::NB), w = q % (C::MB + C::NB);
-        if (w < C::MB)
-          nxt.a[s][w] = *reinterpret_cast<const bf16x8*>(src + (fx + w * 32) * C::ROW_BYTES + roff[s]);
-        else
-          nxt.b[s][w - C::MB] =
-              *reinterpret_cast<const bf16x8*>(src + C::X_BYTES + (fy + (w - C::MB) * 32) * C::ROW_BYTES + roff[s]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-#pragma unroll
-  for (int p = 0; p < C::NSTAGE - 1; ++p)
-    if (p < nk) issue(p);
-  wait_stage(0, C::NSTAGE - 2);
-  phase_barrier();
-  Frags<C> fa, fb;
-  read(0, fa);
-  // steady state: slice kt + NSTAGE - 1 (the one refilled) is whole
-  const int n_full = kdim / C::BK;
-  int kt = 0;
-  for (; kt + C::NSTAGE < n_full; kt += 2) {
-    step_full(kt, fa, fb);
-    step_full(kt + 1, fb, fa);
-  }
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, fa, fb);
-    step(kt + 1, fb, fa);
-  }
-  if (kt < nk) step(kt, fa, fb);
-  __syncthreads();
-}
 
 // ---------------------------------------------------------------------------
 // bf16 main loop on 64-wide k slices in two LDS stages.
 //
 // A stage row holds 64 k values = 128 bytes = eight 16-byte chunks, so one
 // global_load_lds instruction of a wave moves 8 rows x 128 bytes, i.e. whole
-// cache lines: half the texture-address and L1 requests per byte of the
+// cache lines: half the texture-address and L1 requests per byte of a
 // 32-wide layout, whose instructions touch sixteen half lines.  Chunk c of
 // row r sits in slot c ^ ((r >> 1) & 7): with 64 four-byte banks the sixteen
 // lanes of a ds_read_b128 quarter-wave (sixteen consecutive rows, one chunk)
@@ -845,10 +382,11 @@ __device__ __forceinline__ void tile_k64_prologue(const bf16_t* __restrict__ X, 
   K64Loader<C>(X, ldx, xrows, Y, ldy, yrows, kdim).prologue(smem);
 }
 
-// Same contract as tile_mma_dma (kdim a multiple of 8; k past kdim reads as
-// zero; rows past xrows / yrows give garbage outputs to discard; ends with a
-// barrier), except that offsets are in bytes: BM * ldx * 2 and BN * ldy * 2
-// must stay below 2^31.  PRE (PIPE = 2 only): the prologue was issued by
+// Computes the BM x BN tile over k in [0, kdim) (kdim a multiple of 8).  k
+// past kdim reads as zero; rows past xrows / yrows give outputs that callers
+// must discard (select, never multiply).  Byte offsets BM * ldx * 2 and
+// BN * ldy * 2 must stay below 2^31.  Ends with a barrier after which the LDS
+// may be reused.  PRE (PIPE = 2 only): the prologue was issued by
 // tile_k64_prologue with the same arguments; the loop starts by waiting for
 // every outstanding vector memory operation (stores count on this GPU).
 template <class C, bool PRE = false>
@@ -1132,9 +670,7 @@ __device__ __forceinline__ void run_mma(Tile<C>& t, const typename C::TIn* X, in
 template <class C, bool PRE = false>
 __device__ __forceinline__ void run_mma(DmaTile<C>& t, const bf16_t* X, int64_t ldx, int xrows, const bf16_t* Y,
                                         int64_t ldy, int yrows, int kdim, char* smem) {
-  if constexpr (C::BK == 64) tile_mma_k64<C, PRE>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
-  else if constexpr (C::NWAVES == 4) tile_mma_sp<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
-  else tile_mma_dma<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
+  tile_mma_k64<C, PRE>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
 }
 
 }  // namespace ckl
