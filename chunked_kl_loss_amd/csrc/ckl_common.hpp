@@ -31,6 +31,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// The value itself, opaque to the optimizer: a cheap expression derived from
+// it inside a loop is computed there instead of being hoisted out and held in
+// a register across the loop (where it would crowd out the accumulators).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Merge two online log-sum-exp states kept in base-2 units: (m, s) stands for

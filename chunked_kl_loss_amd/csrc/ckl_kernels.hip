@@ -194,12 +194,12 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
 // (m, s): the base-2 log-sum-exp state of row t over the split.
 //
 // STORE (the fused forward + backward): the exponentials the running sum is
-// built from are also kept.  Every lane owns, per token, the vocabulary rows
-// of one (wave_m, lane >> 5) group of each tile and a running maximum m over
-// them (base 2).  It stores u = 2^(z log2e - m) <= 1 at G[t][v] (zero for
-// v >= V) and m itself at mtab[((vt WAVES_M + wave_m) 2 + (lane >> 5)) ldm + t],
-// so that exp(z - LSE) = u 2^(m - LSE log2e) can be formed once the LSE is
-// known, without recomputing z.  No overflow: u <= 1 and m <= LSE log2e.
+// built from are also kept.  The lanes holding one token's column of a wave's
+// WM vocabulary rows keep a common running maximum m over them (base 2); they
+// store u = 2^(z log2e - m) <= 1 at G[t][v] (zero for v >= V) and m itself at
+// mtab[(vt WAVES_M + wave_m) ldm + t], so that exp(z - LSE) = u 2^(m - LSE
+// log2e) can be formed once the LSE is known, without recomputing z.  No
+// overflow: u <= 1 and m <= LSE log2e.
 constexpr int kGroupT = 8;
 
 template <class C, bool STORE>
@@ -209,9 +209,22 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
     float* __restrict__ mtab, int64_t ldm) {
   using TIn = typename C::TIn;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TileT = typename C::TileT;
+  using L = typename TileT::L;
+  constexpr int MBK = TileT::MBK, NBK = TileT::NBK, BLK = L::BLK, RPB = L::RPB;
+  constexpr int GLANES = 64 / L::GROUPS;  // lanes l, l + GLANES, ... hold the rows of one column
+  // Lane group g owns column block nb = g: it keeps that token's running LSE
+  // state and its place in the sorted teacher list, the other groups only
+  // contribute partial maxima, sums and gathered logits for the tile.
+  static_assert(NBK == L::GROUPS && GLANES == BLK, "one column block per lane group");
+  // Between tiles the entry after the owner's next teacher index waits in
+  // LDS after the k-loop stages, fetched by a global->LDS load: a later
+  // epilogue reads it there, so no epilogue waits for a global load of its own
+  // (which would also wait for the next tile's slices and this tile's stores).
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES + C::NTHREADS * 4];
+  int* s_nxt2 = reinterpret_cast<int*>(smem + C::LDS_BYTES);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
   int tblock, split;
@@ -219,24 +232,25 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   const int t0 = tblock * C::BN;
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
+  const int own_nb = lane / GLANES;
+  const int own_tok = t0 + wave_n * C::WN + own_nb * BLK + (lane & (BLK - 1));
 
-  int tok[C::NB], cur[C::NB], nxt[C::NB];
-  float rm[C::NB], rs[C::NB];
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    tok[nb] = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
-    rm[nb] = -INFINITY;
-    rs[nb] = 0.f;
-    cur[nb] = K;
-    nxt[nb] = kIdxEnd;
-    if (tok[nb] < T) {
-      const int* row = idx_s + (int64_t)tok[nb] * K;
-      cur[nb] = lower_bound_row(row, K, vt0 * C::BM);
-      nxt[nb] = cur[nb] < K ? row[cur[nb]] : kIdxEnd;
+  // the owner's state: running maximum and sum (base 2), position cur of the
+  // next teacher index nxt at or after this split's first row
+  float rm = -INFINITY, rs = 0.f;
+  int cur = K, nxt = kIdxEnd;
+  {
+    int nxt2 = kIdxEnd;
+    if (own_tok < T) {
+      const int* row = idx_s + (int64_t)own_tok * K;
+      cur = lower_bound_row(row, K, vt0 * C::BM);
+      nxt = cur < K ? row[cur] : kIdxEnd;
+      nxt2 = cur + 1 < K ? row[cur + 1] : kIdxEnd;
     }
+    s_nxt2[threadIdx.x] = nxt2;
   }
 
-  typename C::TileT tile;
+  TileT tile;
   // With the substep loop, the next tile's first two slices are issued right
   // after a tile's k loop, so that their latency overlaps this tile's epilogue
   // (registers and global memory only; the LDS stages are untouched).
@@ -253,83 +267,107 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     } else {
       run_mma(tile, W + (int64_t)v0 * d, d, V - v0, Ht0, d, T - t0, d, smem);
     }
+    // (without the prefetch, the k loop need not have waited for every
+    // load: the teacher-list entries loaded into LDS must have landed)
+    if constexpr (!kAhead) wait_vmcnt<0>();
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
+    for (int nb = 0; nb < NBK; ++nb) {
+      const int src = (lane & (GLANES - 1)) + nb * GLANES;  // the owner of column nb
+      const bool own = own_nb == nb;
+      const int tok = opaque(t0 + wave_n * C::WN + nb * BLK + (lane & (BLK - 1)));
       float mx = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
+      for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vbase + mb * 32 + acc_row(r, lane);
+        for (int r = 0; r < RPB; ++r) {
+          const int v = vbase + mb * BLK + L::row_in(r, lane);
           if (v < V) mx = fmaxf(mx, tile.acc[mb][nb][r] * kLog2e);
         }
-      const float mn = fmaxf(rm[nb], mx);
-      // logits at the teacher indices of this row that fall in this tile
-      while (nxt[nb] < vend) {
-        const int vl = nxt[nb] - vbase;
-        if (vl >= 0 && vl < C::WM) {
-          const int rr = vl & 31;
-          if (((rr >> 2) & 1) == (lane >> 5)) {
-            const int sel = (vl >> 5) * 16 + (rr >> 3) * 4 + (rr & 3);
-            float val = 0.f;
 #pragma unroll
-            for (int q = 0; q < C::MB * 16; ++q) val = (q == sel) ? tile.acc[q / 16][nb][q % 16] : val;
-            zg_s[(int64_t)tok[nb] * K + cur[nb]] = val;
+      for (int o = GLANES; o < 64; o *= 2) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float crm = __shfl(rm, src);
+      const float mn = fmaxf(crm, mx);
+      // logits at the teacher indices of this token that fall in this tile;
+      // the lanes of the column walk the list together
+      int ccur = __shfl(cur, src), cnxt = __shfl(nxt, src);
+      if (cnxt < vend) {
+        auto gather = [&]() {  // teacher entry ccur (index cnxt) lies in this tile
+          const int vl = cnxt - vbase;
+          if (vl >= 0 && vl < C::WM) {
+            const int rr = vl % BLK;
+            if (L::group_of(rr) == own_nb) {
+              const int sel = (vl / BLK) * RPB + L::reg_of(rr);
+              float val = 0.f;
+#pragma unroll
+              for (int q = 0; q < MBK * RPB; ++q) val = (q == sel) ? tile.acc[q / RPB][nb][q % RPB] : val;
+              zg_s[(int64_t)tok * K + ccur] = val;
+            }
           }
+          ++ccur;
+        };
+        gather();
+        // the entry after it waits in LDS; a second hit in one tile (rare)
+        // reads the list directly
+        cnxt = s_nxt2[wave * 64 + src];
+        while (cnxt < vend) {
+          gather();
+          cnxt = ccur < K ? idx_s[(int64_t)tok * K + ccur] : kIdxEnd;
         }
-        ++cur[nb];
-        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok[nb] * K + cur[nb]] : kIdxEnd;
+        if (own) {
+          cur = ccur;
+          nxt = cnxt;
+          if (ccur + 1 < K)
+            lds_dma4(idx_s + (int64_t)tok * K + ccur + 1, s_nxt2 + wave * 64);
+          else
+            s_nxt2[threadIdx.x] = kIdxEnd;
+        }
       }
       float ssum = 0.f;
       if (mn != -INFINITY) {
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = vbase + mb * 32 + acc_row(r, lane);
+          for (int r = 0; r < RPB; ++r) {
+            const int v = vbase + mb * BLK + L::row_in(r, lane);
             const float u = v < V ? fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn) : 0.f;
             ssum += u;
             if constexpr (STORE) tile.acc[mb][nb][r] = u;
           }
-        rs[nb] = rs[nb] * fast_exp2(rm[nb] - mn) + ssum;
-        rm[nb] = mn;
+#pragma unroll
+        for (int o = GLANES; o < 64; o *= 2) ssum += __shfl_xor(ssum, o);
+        if (own) {
+          rs = rs * fast_exp2(rm - mn) + ssum;
+          rm = mn;
+        }
       } else if constexpr (STORE) {
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
+          for (int r = 0; r < RPB; ++r) tile.acc[mb][nb][r] = 0.f;
       }
       if constexpr (STORE) {
-        const int64_t trow = tok[nb];
+        // registers 4i .. 4i + 3 of a block hold four consecutive rows
+        const int64_t trow = tok;
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int vcol = vbase + mb * 32 + 8 * i + 4 * (lane >> 5);
+          for (int i = 0; i < RPB / 4; ++i) {
+            const int vcol = vbase + mb * BLK + L::row_in(4 * i, lane);
             store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
                         tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
           }
-        mtab[(((int64_t)vt * C::WAVES_M + wave_m) * 2 + (lane >> 5)) * ldm + trow] = mn;
+        if (own) mtab[((int64_t)vt * C::WAVES_M + wave_m) * ldm + trow] = mn;
       }
     }
   }
 
-  // lanes l and l ^ 32 hold the same token over different vocabulary rows
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const float om = __shfl_xor(rm[nb], 32);
-    const float os = __shfl_xor(rs[nb], 32);
-    lse2_merge(rm[nb], rs[nb], om, os);
-  }
-  // then across the WAVES_M waves sharing the same tokens
+  // merge across the WAVES_M waves sharing the same tokens (each lane owns
+  // the column wave_n WN + lane); no load into LDS outlives the workgroup
+  wait_vmcnt<0>();
   float2* red = reinterpret_cast<float2*>(smem);  // [WAVES_M][BN]
-  if (lane < 32) {
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-      red[wave_m * C::BN + wave_n * C::WN + nb * 32 + lane] = make_float2(rm[nb], rs[nb]);
-  }
+  red[wave_m * C::BN + wave_n * C::WN + lane] = make_float2(rm, rs);
   __syncthreads();
   for (int i = threadIdx.x; i < C::BN; i += C::NTHREADS) {
     float m = -INFINITY, s = 0.f;
@@ -513,7 +551,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   using TIn = typename C::TIn;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
   int tblock, split;
@@ -628,22 +666,21 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
   const int t0 = blockIdx.y * 128, v0 = blockIdx.x * 128;
   const int c = threadIdx.x % CPR, rr = threadIdx.x / CPR;
   const int vc = v0 + c * E;  // first vocabulary entry of this thread's chunks
-  // all E entries of a chunk share the tile and the wave row block; entries
-  // with bit 2 of v clear / set belong to lane groups h = 0 / 1
-  const int64_t grp = ((int64_t)(vc / tile_m) * (tile_m / wave_rows) + (vc % tile_m) / wave_rows) * 2;
+  // all E entries of a chunk share the tile and the wave row block, whose
+  // maximum m the forward kept in mtab
+  const int64_t grp = (int64_t)(vc / tile_m) * (tile_m / wave_rows) + (vc % tile_m) / wave_rows;
   constexpr int NR = 128 / RPP;  // rows per thread
   // all loads first (the in-place stores would otherwise order each row's
   // load after the previous row's store, leaving one load in flight)
   using VT = typename std::conditional<kBF16, u32x4, f32x4>::type;
   VT x[NR];
-  float f0[NR], f1[NR];
+  float f0[NR];
   bool ok[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     const int t = t0 + rr + j * RPP;
     x[j] = *reinterpret_cast<const VT*>(G + (int64_t)t * ldG + vc);
     f0[j] = 0.f;
-    f1[j] = 0.f;
     ok[j] = false;
     if (t < rows) {
       const float sc = srow[t];
@@ -652,7 +689,6 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
         const float coef = sc * Mrow[t];
         const float l2 = lse[t] * kLog2e;
         f0[j] = coef * fast_exp2(mtab[grp * ldm + t] - l2);
-        f1[j] = coef * fast_exp2(mtab[(grp + 1) * ldm + t] - l2);
       }
     }
   }
@@ -669,9 +705,8 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
       for (int e = 0; e < E; e += 2) {
         const float u0 = bf16_bits_to_f32(x[j][e >> 1] & 0xffffu);
         const float u1 = bf16_bits_to_f32(x[j][e >> 1] >> 16);
-        const float fe = (e & 4) ? f1[j] : f0[j];
-        const float g0 = (ok[j] && vc + e < V) ? u0 * fe : 0.f;
-        const float g1 = (ok[j] && vc + e + 1 < V) ? u1 * fe : 0.f;
+        const float g0 = (ok[j] && vc + e < V) ? u0 * f0[j] : 0.f;
+        const float g1 = (ok[j] && vc + e + 1 < V) ? u1 * f0[j] : 0.f;
         y[e >> 1] = pack_bf16x2(g0, g1);
       }
       *reinterpret_cast<u32x4*>(gp) = y;
@@ -680,7 +715,7 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
     } else {
       f32x4 y;
 #pragma unroll
-      for (int e = 0; e < E; ++e) y[e] = (ok[j] && vc + e < V) ? x[j][e] * (((vc + e) & 4) ? f1[j] : f0[j]) : 0.f;
+      for (int e = 0; e < E; ++e) y[e] = (ok[j] && vc + e < V) ? x[j][e] * f0[j] : 0.f;
       *reinterpret_cast<f32x4*>(gp) = y;
 #pragma unroll
       for (int e = 0; e < E; ++e) tr[(c * E + e) * LDT + i] = y[e];
@@ -776,7 +811,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
                                                                  GemmProblem<typename C::TIn> p1) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
   // Each problem is spread over all XCDs on its own (problem 1 starts at a
@@ -813,7 +848,9 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
   int tm, tn;
   grouped_mn(bid, tiles_m, per_batch / tiles_m, kGroupM, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  typename C::TileT tile;
+  using TileT = typename C::TileT;
+  using L = typename TileT::L;
+  TileT tile;
   run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
   if constexpr (C::WAVES_M == 2 && C::BM * C::BN * 2 <= C::LDS_BYTES) {
     // The fp32 tile goes out through LDS, one half (the rows of one wave_m)
@@ -823,17 +860,24 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
     // instruction (measured ~1.6x slower for the fp32 dW update).
     float* st = reinterpret_cast<float*>(smem);
     constexpr int HALF = C::BM / 2;
+    // the lane groups of a column write rows 4 apart: their columns are
+    // offset by BLK per group so that one store touches distinct banks
+    // (16-byte runs stay contiguous for the reads below)
+    auto stage_swz = [](int ml) { return ((ml >> 2) & (L::GROUPS - 1)) * L::BLK; };
     const bool vec_ok = (ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (wave_m == half) {
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < TileT::MBK; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            const int nl = wave_n * C::WN + nb * 32 + (lane & 31);
+          for (int nb = 0; nb < TileT::NBK; ++nb) {
+            const int nl = wave_n * C::WN + nb * L::BLK + (lane & (L::BLK - 1));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[(mb * 32 + acc_row(r, lane)) * C::BN + nl] = tile.acc[mb][nb][r];
+            for (int r = 0; r < L::RPB; ++r) {
+              const int ml = mb * L::BLK + L::row_in(r, lane);
+              st[ml * C::BN + (nl ^ stage_swz(ml))] = tile.acc[mb][nb][r];
+            }
           }
       }
       __syncthreads();
@@ -862,7 +906,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
         const int m = m0 + half * HALF + ml, n = n0 + c4;
         if (m >= M || n >= N) continue;
-        const float* sv = st + ml * C::BN + c4;
+        const float* sv = st + ml * C::BN + (c4 ^ stage_swz(ml));
         float* o = out + (int64_t)m * ldo + n;
         if (vec_ok && n + 4 <= N) {
           *reinterpret_cast<f32x4*>(o) = *reinterpret_cast<const f32x4*>(sv) + old[j];
@@ -875,13 +919,13 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
     }
   } else {
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int mb = 0; mb < TileT::MBK; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int n = n0 + wave_n * C::WN + nb * 32 + (lane & 31);
+      for (int nb = 0; nb < TileT::NBK; ++nb) {
+        const int n = n0 + wave_n * C::WN + nb * L::BLK + (lane & (L::BLK - 1));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wave_m * C::WM + mb * 32 + acc_row(r, lane);
+        for (int r = 0; r < L::RPB; ++r) {
+          const int m = m0 + wave_m * C::WM + mb * L::BLK + L::row_in(r, lane);
           if (m < M && n < N) {
             float* o = out + (int64_t)m * ldo + n;
             const float a = tile.acc[mb][nb][r];
@@ -1151,7 +1195,7 @@ hipError_t launch_splitk_sum(const float* part, int64_t pstride, int S, int64_t 
 int tile_rows_m(int in_bf16) { return in_bf16 ? CfgBF16::BM : CfgF32::BM; }
 int tile_rows_n(int in_bf16) { return in_bf16 ? CfgBF16::BN : CfgF32::BN; }
 int gemm_tile(int in_bf16) { return in_bf16 ? CfgBF16Gemm::BM : CfgF32::BM; }
-int lse_groups_per_tile(int in_bf16) { return in_bf16 ? 2 * CfgBF16::WAVES_M : 2 * CfgF32::WAVES_M; }
+int lse_groups_per_tile(int in_bf16) { return in_bf16 ? CfgBF16::WAVES_M : CfgF32::WAVES_M; }
 static_assert(CfgBF16Gemm::BM == CfgBF16Gemm::BN && CfgF32::BM == CfgF32::BN, "square contraction tiles");
 
 }  // namespace ckl

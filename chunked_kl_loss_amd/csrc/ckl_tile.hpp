@@ -70,9 +70,25 @@ struct TileCfg {
 //   col n = wave_n*WN + nb*32 + l%32.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// The wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Accumulator layout of the 32 x 32 blocks, as the epilogues see it: BLK x
+// BLK blocks, RPB registers per block and lane; GROUPS lanes (l, l ^ 32) hold
+// the rows of one column; register r of lane l sits in block row row_in(r, l);
+// block row rr lives in lane group group_of(rr), register reg_of(rr).
+struct AccLayout32 {
+  static constexpr int BLK = 32, RPB = 16, GROUPS = 2;
+  static __device__ __forceinline__ int row_in(int r, int lane) { return acc_row(r, lane); }
+  static __device__ __forceinline__ int group_of(int rr) { return (rr >> 2) & 1; }
+  static __device__ __forceinline__ int reg_of(int rr) { return (rr >> 3) * 4 + (rr & 3); }
+};
+
 template <class C>
 struct Tile {
   using TIn = typename C::TIn;
+  using L = AccLayout32;
+  static constexpr int MBK = C::MB, NBK = C::NB;
   f32x16 acc[C::MB][C::NB];
 };
 
@@ -88,7 +104,7 @@ __device__ __forceinline__ void tile_mma(Tile<C>& tile, const typename C::TIn* _
   using TIn = typename C::TIn;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
 
@@ -204,6 +220,11 @@ __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
+// global_load_lds_dword: 4 bytes per lane into LDS at `lds` + 4 * lane
+// (`lds` wave-uniform).
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
 
 // Raw buffer resource (stride 0) over `bytes` bytes from `base`: loads at
 // offsets past `bytes` return zeros.  Word 3 is the gfx9-family default for
@@ -229,6 +250,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Accumulators of one wave's MB x NB blocks of 32 x 32 outputs.
 template <class C>
 struct DmaTile {
+  using L = AccLayout32;
+  static constexpr int MBK = C::MB, NBK = C::NB;
   f32x16 acc[C::MB][C::NB];
 };
 
@@ -316,7 +339,10 @@ struct K64Loader {
   const bf16_t* X;
   const bf16_t* Y;
   __amdgpu_buffer_rsrc_t rx, ry;  // (unused, and dropped by the compiler, when BUF = 0)
-  uint32_t off[C::LOADS_PER_STAGE];
+  // BUF: byte offsets of this lane's first X and Y loads; load i adds i steps
+  // (the steps are workgroup-uniform).  Otherwise element offsets of every load.
+  uint32_t off[C::BUF ? 2 : C::LOADS_PER_STAGE];
+  uint32_t xstep, ystep;
   int wave, lchunk, kdim;
   __device__ __forceinline__ K64Loader(const bf16_t* X_, int64_t ldx, int xrows, const bf16_t* Y_, int64_t ldy,
                                        int yrows, int kdim_)
@@ -324,21 +350,27 @@ struct K64Loader {
         Y(Y_),
         rx(make_rsrc(X_, (uint32_t)(min(xrows, C::BM) * ldx * 2))),
         ry(make_rsrc(Y_, (uint32_t)(min(yrows, C::BN) * ldy * 2))),
+        xstep((uint32_t)(C::NWAVES * 8 * ldx * 2)),
+        ystep((uint32_t)(C::NWAVES * 8 * ldy * 2)),
         kdim(kdim_) {
     const int lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = wave_id();
     const int lrow = lane >> 3;
     lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
+    if constexpr (C::BUF) {
+      off[0] = (uint32_t)((wave * 8 + lrow) * ldx * 2 + lchunk * 16);
+      off[1] = (uint32_t)((wave * 8 + lrow) * ldy * 2 + lchunk * 16);
+    } else {
 #pragma unroll
-    for (int i = 0; i < C::X_LOADS; ++i) {
-      const int row = (wave + i * C::NWAVES) * 8 + lrow;
-      off[i] = C::BUF ? (uint32_t)(row * ldx * 2 + lchunk * 16) : (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-    }
+      for (int i = 0; i < C::X_LOADS; ++i) {
+        const int row = (wave + i * C::NWAVES) * 8 + lrow;
+        off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
+      }
 #pragma unroll
-    for (int i = 0; i < C::Y_LOADS; ++i) {
-      const int row = (wave + i * C::NWAVES) * 8 + lrow;
-      off[C::X_LOADS + i] =
-          C::BUF ? (uint32_t)(row * ldy * 2 + lchunk * 16) : (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
+      for (int i = 0; i < C::Y_LOADS; ++i) {
+        const int row = (wave + i * C::NWAVES) * 8 + lrow;
+        off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
+      }
     }
   }
   __device__ __forceinline__ char* lds_at(char* smem, int kt, int i) const {
@@ -352,8 +384,9 @@ struct K64Loader {
   __device__ __forceinline__ void dma(char* smem, int kt, int i, bool whole) const {
     const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
     if constexpr (C::BUF) {
-      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? off[i] : kOutOfRange, (uint32_t)(kt * C::BK * 2),
-                  lds_at(smem, kt, i));
+      // the offset is formed here rather than kept per load in registers
+      const uint32_t o = i < C::X_LOADS ? off[0] + (uint32_t)i * xstep : off[1] + (uint32_t)(i - C::X_LOADS) * ystep;
+      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? o : kOutOfRange, (uint32_t)(kt * C::BK * 2), lds_at(smem, kt, i));
     } else {
       const bf16_t* src = (i < C::X_LOADS ? X : Y) + kt * C::BK + off[i];
       lds_dma16(in ? (const void*)src : (const void*)kZeroChunk, lds_at(smem, kt, i));
@@ -397,7 +430,7 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
   static_assert(!PRE || C::PIPE == 2, "prologue issued ahead only for the substep pipeline");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
   const int wave_n = wave % C::WAVES_N;
 
