@@ -293,7 +293,7 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
 }
 
 struct FusedWs {
-  size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, s, Ht, Wt, G, Gt, mtab, dHp, dW, total;
+  size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, s, Ht, Wt, U, G, Gt, mtab, dHp, dW, total;
 };
 FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   FusedWs w{};
@@ -311,6 +311,9 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   w.s = take(q.Tp * 4);
   w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
   w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
+  // bf16: u of a chunk in the forward's tile order, laid out as G and G^T
+  // by gpass_tiles (fp32 keeps u in G itself)
+  w.U = q.in_bf16 ? take((size_t)q.Cs * q.Vp * q.esz) : 0;
   w.G = take((size_t)q.Cs * (q.Vp + kLdPad) * q.esz);
   w.Gt = take((size_t)q.Vp * (kDwChunks * q.Cs + kLdPad) * q.esz);
   w.mtab = take((size_t)q.groups * q.Cs * 4);
@@ -548,6 +551,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   float* srow = (float*)(b + w.s);
   char* Ht = b + w.Ht;
   char* Wt = b + w.Wt;
+  char* U = b + w.U;
   char* G = b + w.G;
   char* Gt = b + w.Gt;
   float* mtab = (float*)(b + w.mtab);
@@ -588,7 +592,8 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
                     return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
-                                               b + w.part, (int)q.c_splits, (int)q.c_tps, G, ldG, mtab, q.Cs, st);
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, q.in_bf16 ? U : G, ldG,
+                                               mtab, q.Cs, st);
                   }),
             "fwd_lse (store)");
     HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
@@ -600,6 +605,9 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
             "fwd_rows");
     HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
                   [&] {
+                    if (q.in_bf16)
+                      return ckl::launch_gpass_tiles(U, (int)(q.Vp / q.BM), rows_p / (int)q.BN, G, ldG, Gtc, ldGt,
+                                                     mtab, q.Cs, srow + tb0, M + tb0, lse + tb0, rows, V, st);
                     return ckl::launch_gpass(q.in_bf16, G, ldG, Gtc, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
                                              rows, rows_p, V, (int)q.Vp, st);
                   }),

@@ -24,6 +24,18 @@
 
 namespace ckl {
 
+// ----------------------------------------------------------- configurations --
+// bf16: 256 x 256 tiles on 64-wide k slices, 8 waves (2 per SIMD, so one
+// wave's loads, barriers and epilogue overlap the other's MFMAs).  The fused
+// logit kernels pipeline fragment reads per k16 substep, keeping for their
+// epilogue state the registers the plain dH / dW contraction spends on
+// fragments double-buffered per half stage.  fp32 (small problems):
+// 128 x 128 tiles, register-staged loads.
+using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
+using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
+using CfgBF16Gemm = Dma64Cfg<256, 256, 128, 64, 1>;
+using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
+
 // ---------------------------------------------------------------- helpers --
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -196,10 +208,11 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict_
 // STORE (the fused forward + backward): the exponentials the running sum is
 // built from are also kept.  The lanes holding one token's column of a wave's
 // WM vocabulary rows keep a common running maximum m over them (base 2); they
-// store u = 2^(z log2e - m) <= 1 at G[t][v] (zero for v >= V) and m itself at
+// store u = 2^(z log2e - m) <= 1 (zero for v >= V) and m itself at
 // mtab[(vt WAVES_M + wave_m) ldm + t], so that exp(z - LSE) = u 2^(m - LSE
 // log2e) can be formed once the LSE is known, without recomputing z.  No
-// overflow: u <= 1 and m <= LSE log2e.
+// overflow: u <= 1 and m <= LSE log2e.  fp32 stores u at G[t][v]; bf16 in
+// tile order (see the store below), which gpass_tiles_kernel reads.
 constexpr int kGroupT = 8;
 
 template <class C, bool STORE>
@@ -217,6 +230,10 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   // state and its place in the sorted teacher list, the other groups only
   // contribute partial maxima, sums and gathered logits for the tile.
   static_assert(NBK == L::GROUPS && GLANES == BLK, "one column block per lane group");
+  // bf16 keeps u in tile order (whole 1 KiB stores; gpass_tiles_kernel lays
+  // it out as G and G^T), fp32 at G[t][v] directly
+  constexpr bool kTileU = sizeof(TIn) == 2;
+  static_assert(!kTileU || (RPB == 16 && C::BM == 256 && C::BN == 256), "tile order of the bf16 configuration");
   // Between tiles the entry after the owner's next teacher index waits in
   // LDS after the k-loop stages, fetched by a global->LDS load: a later
   // epilogue reads it there, so no epilogue waits for a global load of its own
@@ -348,16 +365,33 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
           for (int r = 0; r < RPB; ++r) tile.acc[mb][nb][r] = 0.f;
       }
       if constexpr (STORE) {
-        // registers 4i .. 4i + 3 of a block hold four consecutive rows
         const int64_t trow = tok;
+        if constexpr (kTileU) {
+          // u in tile order: the tile's (tblock, vt) block of BM x BN entries,
+          // within it 1 KiB per (wave, mb, nb, h), lane l at 16 l: registers
+          // 8h .. 8h + 7 of the lane's block (mb, nb)
+          TIn* ut = G + ((int64_t)tblock * n_vtiles + vt) * (C::BM * C::BN);
 #pragma unroll
-        for (int mb = 0; mb < MBK; ++mb)
+          for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-          for (int i = 0; i < RPB / 4; ++i) {
-            const int vcol = vbase + mb * BLK + L::row_in(4 * i, lane);
-            store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
-                        tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
-          }
+            for (int h = 0; h < 2; ++h) {
+              u32x4 y;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                y[e] = pack_bf16x2(tile.acc[mb][nb][8 * h + 2 * e], tile.acc[mb][nb][8 * h + 2 * e + 1]);
+              *reinterpret_cast<u32x4*>(ut + ((((wave * MBK + mb) * NBK + nb) * 2 + h) * 64 + lane) * 8) = y;
+            }
+        } else {
+          // registers 4i .. 4i + 3 of a block hold four consecutive rows
+#pragma unroll
+          for (int mb = 0; mb < MBK; ++mb)
+#pragma unroll
+            for (int i = 0; i < RPB / 4; ++i) {
+              const int vcol = vbase + mb * BLK + L::row_in(4 * i, lane);
+              store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
+                          tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
+            }
+        }
         if (own) mtab[((int64_t)vt * C::WAVES_M + wave_m) * ldm + trow] = mn;
       }
     }
@@ -739,6 +773,104 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
   }
 }
 
+// bf16: u arrives in the forward's tile order (one 256 x 256 token x
+// vocabulary tile = 128 KiB, whole 1 KiB runs per wave store).  One block per
+// half tile (128 tokens: the forward waves with wave_n in {2 th, 2 th + 1},
+// four runs of 16 KiB) reads it in 16-byte chunks, forms g as above and
+// stages it in LDS as [t][v] (rows of 512 bytes; the 16-byte chunk c of row t
+// sits at c ^ (t / 8), so that eight-row column reads spread over the banks),
+// then writes G rows and, through 8 x 8 register transposes, G^T rows, in
+// 512- and 256-byte runs.  64 KiB of LDS: two blocks per CU, one reading while
+// the other writes.  HBM traffic 3 elements per entry, in whole cache lines.
+__global__ __launch_bounds__(512) void gpass_tiles_kernel(const bf16_t* __restrict__ U, int n_vtiles,
+                                                          bf16_t* __restrict__ G, int64_t ldG, bf16_t* __restrict__ Gt,
+                                                          int64_t ldGt, const float* __restrict__ mtab, int64_t ldm,
+                                                          const float* __restrict__ srow,
+                                                          const float* __restrict__ Mrow,
+                                                          const float* __restrict__ lse, int rows, int V) {
+  using C = CfgBF16;
+  static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128 && C::WN == 64 && C::MB == 4 && C::NB == 2 &&
+                    C::WAVES_M == 2 && C::WAVES_N == 4,
+                "tile order written by fwd_lse_kernel");
+  __shared__ __attribute__((aligned(16))) uint16_t tr[128 * 256];
+  __shared__ float fs[2][128];  // g / u per (wave_m, token): s_t M_t 2^(m - LSE_t log2e), 0 for no gradient
+  const int vt = blockIdx.x, tb = blockIdx.y >> 1, th = blockIdx.y & 1;
+  const int t0 = tb * 256 + th * 128, v0 = vt * 256;
+  const int tid = threadIdx.x;
+  const u32x4* ut = reinterpret_cast<const u32x4*>(U + ((int64_t)tb * n_vtiles + vt) * (256 * 256));
+  auto phys = [](int t, int c) { return c ^ ((t >> 3) & 31); };
+  // wave w of the forward wrote its 16 KiB (1024 chunks) at chunk 1024 w;
+  // this half holds waves 2 th, 2 th + 1 (wave_m 0) and 4 + 2 th, 5 + 2 th
+  auto src_chunk = [&](int c) {
+    const int p = c >> 10;
+    return (((p & 1) + 2 * th + 4 * (p >> 1)) << 10) + (c & 1023);
+  };
+  u32x4 x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = ut[src_chunk(j * 512 + tid)];
+  if (tid < 256) {
+    const int wm = tid >> 7, tl = tid & 127, t = t0 + tl;
+    float f = 0.f;
+    if (t < rows) {
+      const float sc = srow[t];
+      if (sc != 0.f) f = sc * Mrow[t] * fast_exp2(mtab[((int64_t)vt * C::WAVES_M + wm) * ldm + t] - lse[t] * kLog2e);
+    }
+    fs[wm][tl] = f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = j * 512 + tid;
+    const int p = c >> 10, cw = c & 1023;
+    const int lane = cw & 63, h = (cw >> 6) & 1, nb = (cw >> 7) & 1, mb = (cw >> 8) & 3, wm = p >> 1;
+    const int tl = (p & 1) * 64 + nb * 32 + (lane & 31);
+    const int vl = wm * 128 + mb * 32 + 16 * h + 4 * (lane >> 5);  // elements 0-3: vl.., 4-7: vl + 8..
+    const float f = fs[wm][tl];
+    // rows past `rows` and masked rows (f = 0) may hold stale u: select,
+    // never multiply, so that they come out as exact zeros
+    uint32_t y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int va = v0 + vl + (e < 2 ? 2 * e : 8 + 2 * (e - 2));
+      const float u0 = bf16_bits_to_f32(x[j][e] & 0xffffu), u1 = bf16_bits_to_f32(x[j][e] >> 16);
+      const float g0 = (f != 0.f && va < V) ? u0 * f : 0.f;
+      const float g1 = (f != 0.f && va + 1 < V) ? u1 * f : 0.f;
+      y[e] = pack_bf16x2(g0, g1);
+    }
+    uint2* row = reinterpret_cast<uint2*>(tr + tl * 256);
+    // 8-byte halves: v = vl .. vl + 3 (chunk vl / 8, half (vl / 4) % 2) and v + 8 (next chunk)
+    row[phys(tl, vl >> 3) * 2 + ((vl >> 2) & 1)] = make_uint2(y[0], y[1]);
+    row[phys(tl, (vl >> 3) + 1) * 2 + ((vl >> 2) & 1)] = make_uint2(y[2], y[3]);
+  }
+  __syncthreads();
+  // G rows: 32 threads per row of 256 entries
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int tl = pass * 16 + (tid >> 5), q = tid & 31;
+    const u32x4 v = reinterpret_cast<const u32x4*>(tr + tl * 256)[phys(tl, q)];
+    *reinterpret_cast<u32x4*>(G + (int64_t)(t0 + tl) * ldG + v0 + q * 8) = v;
+  }
+  // G^T rows: thread (tq, vb) transposes the 8 x 8 block of tokens 8 tq ..,
+  // vocabulary rows 8 vb ..; 16 threads write one 256-byte row run
+  {
+    const int tq = tid & 15, vb = tid >> 4;
+    u32x4 a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = reinterpret_cast<const u32x4*>(tr + (tq * 8 + i) * 256)[vb ^ tq];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // vocabulary rows 2w (low halves) and 2w + 1 (high halves)
+      u32x4 lo, hi;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        lo[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x05040100u);
+        hi[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x07060302u);
+      }
+      *reinterpret_cast<u32x4*>(Gt + (int64_t)(v0 + vb * 8 + 2 * w) * ldGt + t0 + tq * 8) = lo;
+      *reinterpret_cast<u32x4*>(Gt + (int64_t)(v0 + vb * 8 + 2 * w + 1) * ldGt + t0 + tq * 8) = hi;
+    }
+  }
+}
+
 // Teacher columns: g = s_t (M_t 2^(zg log2e - LSE_t log2e) - p), the same
 // fp32 expression the recomputing backward evaluates, rounded once.
 template <typename TIn>
@@ -937,16 +1069,6 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
 }
 
 // ---------------------------------------------------------------- launchers --
-// bf16: 256 x 256 tiles on 64-wide k slices, 8 waves (2 per SIMD, so one
-// wave's loads, barriers and epilogue overlap the other's MFMAs).  The fused
-// logit kernels pipeline fragment reads per k16 substep, keeping for their
-// epilogue state the registers the plain dH / dW contraction spends on
-// fragments double-buffered per half stage.  fp32 (small problems):
-// 128 x 128 tiles, register-staged loads.
-using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
-using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
-using CfgBF16Gemm = Dma64Cfg<256, 256, 128, 64, 1>;
-using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
 template <typename TIn>
 struct CfgOf;
@@ -1161,6 +1283,16 @@ hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldG
   else
     hipLaunchKernelGGL(gpass_kernel<float>, grid, dim3(256), 0, st, (float*)G, ldG, (float*)Gt, ldGt, mtab, ldm, srow,
                        Mrow, lse, rows, V, CfgF32::BM, CfgF32::WM);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gpass_tiles(const void* U, int n_vtiles, int n_tblocks, void* G, int64_t ldG, void* Gt,
+                              int64_t ldGt, const float* mtab, int64_t ldm, const float* srow, const float* Mrow,
+                              const float* lse, int rows, int V, hipStream_t st) {
+  if (n_vtiles < 1 || n_tblocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(gpass_tiles_kernel, dim3(n_vtiles, 2 * n_tblocks), dim3(512), 0, st, (const bf16_t*)U, n_vtiles,
+                     (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm, srow, Mrow, lse, rows, V);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }

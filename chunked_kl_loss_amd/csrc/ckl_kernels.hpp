@@ -47,6 +47,11 @@ hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldG
 // Teacher columns of rows < rows: g = s_t (M_t exp(zg - lse_t) - p), from the
 // fp32 logits kept by the forward, into G and G^T (indices outside [0, V) are
 // skipped).
+// bf16 fused path: G and G^T of a row chunk from u in the forward's tile order
+// (n_tblocks x n_vtiles tiles of 256 x 256).
+hipError_t launch_gpass_tiles(const void* U, int n_vtiles, int n_tblocks, void* G, int64_t ldG, void* Gt,
+                              int64_t ldGt, const float* mtab, int64_t ldm, const float* srow, const float* Mrow,
+                              const float* lse, int rows, int V, hipStream_t st);
 hipError_t launch_gfix(int in_bf16, int rows, int K, int V, const int* idx_s, const float* p_s, const float* zg_s,
                        const float* srow, const float* Mrow, const float* lse, void* G, int64_t ldG, void* Gt,
                        int64_t ldGt, hipStream_t st);
