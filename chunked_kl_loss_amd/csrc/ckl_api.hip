@@ -228,8 +228,8 @@ Plan make_plan(const ckl_problem* p) {
   // dH split-k parts: the count whose tiles finish in the fewest k-steps when
   // dealt to kCUs workgroups in rounds (whole rounds: a launch that holds only
   // dH tiles ends with its slowest round), each part also paying its epilogue.
-  const int64_t gtile = ckl::gemm_tile(q.in_bf16);
-  const int64_t dh_tiles = ceil_div(q.Cs, gtile) * ceil_div(q.d, gtile);
+  const int64_t dh_tiles = ceil_div(q.Cs, (int64_t)ckl::gemm_tile_m(q.in_bf16)) *
+                           ceil_div(q.d, (int64_t)ckl::gemm_tile_n(q.in_bf16));
   const int64_t sh_max = std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, q.Vp / 256));
   int64_t best_cost = -1;
   for (int64_t sh = 1; sh <= sh_max; ++sh) {

@@ -33,7 +33,7 @@ namespace ckl {
 // 128 x 128 tiles, register-staged loads.
 using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
 using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
-using CfgBF16Gemm = Dma64Cfg<256, 256, 128, 64, 1>;
+using CfgBF16Gemm = Dma64Cfg<256, 320, 64, 160, 2>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
 // ---------------------------------------------------------------- helpers --
@@ -984,22 +984,23 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
   using L = typename TileT::L;
   TileT tile;
   run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
-  if constexpr (C::WAVES_M == 2 && C::BM * C::BN * 2 <= C::LDS_BYTES) {
-    // The fp32 tile goes out through LDS, one half (the rows of one wave_m)
-    // at a time, so that each thread reads / writes 16 contiguous bytes of an
+  if constexpr (C::WM * C::BN * 4 <= C::LDS_BYTES) {
+    // The fp32 tile goes out through LDS, the WM rows of one wave_m at a
+    // time, so that each thread reads / writes 16 contiguous bytes of an
     // output row: in the MFMA layout a lane holds one column, and the
     // read-modify-write would take 4-byte accesses to 32 rows per
     // instruction (measured ~1.6x slower for the fp32 dW update).
     float* st = reinterpret_cast<float*>(smem);
-    constexpr int HALF = C::BM / 2;
+    constexpr int PART = C::WM;
     // the lane groups of a column write rows 4 apart: their columns are
     // offset by BLK per group so that one store touches distinct banks
     // (16-byte runs stay contiguous for the reads below)
     auto stage_swz = [](int ml) { return ((ml >> 2) & (L::GROUPS - 1)) * L::BLK; };
+    static_assert(C::BN % (L::GROUPS * L::BLK) == 0, "the swizzle stays inside a row");
     const bool vec_ok = (ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wave_m == half) {
+    for (int part = 0; part < C::WAVES_M; ++part) {
+      if (wave_m == part) {
 #pragma unroll
         for (int mb = 0; mb < TileT::MBK; ++mb)
 #pragma unroll
@@ -1016,9 +1017,10 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
       // Every thread's old values are loaded before any of its stores: loads
       // and stores of one output array would otherwise stay in program order,
       // one round trip per 16 bytes.
-      constexpr int PER = HALF * (C::BN / 4) / C::NTHREADS;
-      constexpr int BATCH = PER < 8 ? PER : 8;  // float4 loads in flight (registers: the other half's acc is live)
-      static_assert(HALF * (C::BN / 4) % C::NTHREADS == 0 && PER % BATCH == 0, "whole float4 batches");
+      constexpr int PER = PART * (C::BN / 4) / C::NTHREADS;
+      // float4 loads in flight (registers: the other parts' accumulators are live)
+      constexpr int BATCH = PER % 8 == 0 ? 8 : PER % 5 == 0 ? 5 : PER % 4 == 0 ? 4 : PER < 8 ? PER : 1;
+      static_assert(PART * (C::BN / 4) % C::NTHREADS == 0 && PER % BATCH == 0, "whole float4 batches");
 #pragma unroll
       for (int j0 = 0; j0 < PER; j0 += BATCH) {
       f32x4 old[BATCH];
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
       for (int jj = 0; jj < BATCH; ++jj) {
         const int i = threadIdx.x + (j0 + jj) * C::NTHREADS;
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
-        const int m = m0 + half * HALF + ml, n = n0 + c4;
+        const int m = m0 + part * PART + ml, n = n0 + c4;
         old[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (beta && vec_ok && m < M && n + 4 <= N)
           old[jj] = *reinterpret_cast<const f32x4*>(out + (int64_t)m * ldo + n);
@@ -1036,7 +1038,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
         const int j = jj;
         const int i = threadIdx.x + (j0 + jj) * C::NTHREADS;
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
-        const int m = m0 + half * HALF + ml, n = n0 + c4;
+        const int m = m0 + part * PART + ml, n = n0 + c4;
         if (m >= M || n >= N) continue;
         const float* sv = st + ml * C::BN + (c4 ^ stage_swz(ml));
         float* o = out + (int64_t)m * ldo + n;
@@ -1076,8 +1078,8 @@ template <>
 struct CfgOf<bf16_t> { using type = CfgBF16; using bwd = CfgBF16Bwd; using gemm = CfgBF16Gemm; };
 template <>
 struct CfgOf<float> { using type = CfgF32; using bwd = CfgF32; using gemm = CfgF32; };
-static_assert(CfgBF16::BM == CfgBF16Gemm::BM && CfgBF16::BN == CfgBF16Gemm::BN && CfgBF16::BM == CfgBF16Bwd::BM &&
-                  CfgBF16::BN == CfgBF16Bwd::BN, "one tile size per dtype");
+static_assert(CfgBF16::BM == CfgBF16Gemm::BM && CfgBF16::BM == CfgBF16Bwd::BM && CfgBF16::BN == CfgBF16Bwd::BN,
+              "row blocks of one size per dtype");
 
 #define CKL_LAUNCH_CHECK() \
   do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
@@ -1326,8 +1328,8 @@ hipError_t launch_splitk_sum(const float* part, int64_t pstride, int S, int64_t 
 
 int tile_rows_m(int in_bf16) { return in_bf16 ? CfgBF16::BM : CfgF32::BM; }
 int tile_rows_n(int in_bf16) { return in_bf16 ? CfgBF16::BN : CfgF32::BN; }
-int gemm_tile(int in_bf16) { return in_bf16 ? CfgBF16Gemm::BM : CfgF32::BM; }
+int gemm_tile_m(int in_bf16) { return in_bf16 ? CfgBF16Gemm::BM : CfgF32::BM; }
+int gemm_tile_n(int in_bf16) { return in_bf16 ? CfgBF16Gemm::BN : CfgF32::BN; }
 int lse_groups_per_tile(int in_bf16) { return in_bf16 ? CfgBF16::WAVES_M : CfgF32::WAVES_M; }
-static_assert(CfgBF16Gemm::BM == CfgBF16Gemm::BN && CfgF32::BM == CfgF32::BN, "square contraction tiles");
 
 }  // namespace ckl

@@ -86,7 +86,8 @@ hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1,
 // Tile extents of the contraction kernels: G blocks are whole tiles.
 int tile_rows_m(int in_bf16);  // vocabulary rows per logit tile (BM)
 int tile_rows_n(int in_bf16);  // token rows per logit tile (BN)
-int gemm_tile(int in_bf16);    // square tile edge of the plain contraction
+int gemm_tile_m(int in_bf16);  // output tile rows of the plain contraction
+int gemm_tile_n(int in_bf16);  // and columns
 // running-maximum groups per logit tile kept by the fused forward
 int lse_groups_per_tile(int in_bf16);
 
