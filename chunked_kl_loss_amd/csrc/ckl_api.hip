@@ -260,7 +260,7 @@ FwdWs fwd_layout(const Plan& q) {
   w.E = take(q.T * 4);
   w.M = take(q.T * 4);
   w.part = take(q.f_splits * q.T * 8);
-  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.blk = take(q.T * 8);  // per-row fp64 loss terms
   w.N = take(4);
   w.bad = take(4);
   w.total = o;
@@ -305,7 +305,7 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   w.E = take(q.T * 4);
   w.M = take(q.T * 4);
   w.part = take(q.c_splits * q.Cs * 8);
-  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.blk = take(q.T * 8);  // per-row fp64 loss terms
   w.N = take(4);
   w.bad = take(4);
   w.s = take(q.Tp * 4);
@@ -334,7 +334,7 @@ CombineWs combine_layout(const Plan& q) {
   w.p_s = take(q.T * q.K * 4);
   w.E = take(q.T * 4);
   w.M = take(q.T * 4);
-  w.blk = take(ceil_div(q.T, 256) * 8);
+  w.blk = take(q.T * 8);  // per-row fp64 loss terms
   w.N = take(4);
   w.bad = take(4);
   w.total = o;
@@ -600,7 +600,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
                   [&] {
                     return ckl::launch_fwd_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K, zg_s + tb0 * K,
                                                 E + tb0, M + tb0, mask ? mask + tb0 : nullptr, lse + tb0,
-                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0 / 256, st);
+                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0, st);
                   }),
             "fwd_rows");
     HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
@@ -640,7 +640,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
             "dH sum");
   }
   HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
-                [&] { return ckl::launch_loss_reduce(blk, (int)ceil_div(q.T, 256), N, loss, st); }),
+                [&] { return ckl::launch_loss_reduce(blk, (int)q.T, N, loss, st); }),
           "loss_reduce");
   if (p->dw_dtype == CKL_BF16)
     HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),

@@ -414,7 +414,10 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   }
 }
 
-// One thread per row: LSE from the split states, l_t, masked fp64 block sum.
+// Sixteen lanes per row: LSE from the split states, l_t = E_t - sum_k p z +
+// M_t LSE, and l_t in fp64 at row_ld[t] for the deterministic mean (0 for
+// masked rows).  Lane j of a row takes splits j, j + 16, .. and teacher
+// entries j, j + 16, ..; the partials merge by shuffles in a fixed order.
 __global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restrict__ part, int S, int T, int K,
                                                            const float* __restrict__ p_s,
                                                            const float* __restrict__ zg_s,
@@ -423,45 +426,48 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restr
                                                            const uint8_t* __restrict__ mask,
                                                            float* __restrict__ lse_out,
                                                            float* __restrict__ row_loss,
-                                                           double* __restrict__ blk_sum) {
-  __shared__ double red[256];
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  double contrib = 0.0;
-  if (t < T) {
-    const bool keep = mask == nullptr || mask[t] != 0;
+                                                           double* __restrict__ row_ld) {
+  const int sub = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = t < T;
+  const bool keep = valid && (mask == nullptr || mask[t] != 0);
+  float m = -INFINITY, s = 0.f;
+  double x = 0.0;
+  if (keep) {
+    for (int sp = sub; sp < S; sp += 16) {
+      const float2 v = part[(int64_t)sp * T + t];
+      lse2_merge(m, s, v.x, v.y);
+    }
+    const float* pr = p_s + (int64_t)t * K;
+    const float* zr = zg_s + (int64_t)t * K;
+    for (int k = sub; k < K; k += 16) x += (double)pr[k] * (double)zr[k];
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o *= 2) {
+    const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
+    lse2_merge(m, s, om, os);
+    x += __shfl_xor(x, o);
+  }
+  if (sub == 0 && valid) {
     float lse = 0.f, l = 0.f;
+    double ld = 0.0;
     if (keep) {
-      float m = -INFINITY, s = 0.f;
-      for (int sp = 0; sp < S; ++sp) {
-        const float2 x = part[(int64_t)sp * T + t];
-        lse2_merge(m, s, x.x, x.y);
-      }
       lse = (m + fast_log2(s)) * kLn2;
-      double x = 0.0;
-      const float* pr = p_s + (int64_t)t * K;
-      const float* zr = zg_s + (int64_t)t * K;
-      for (int k = 0; k < K; ++k) x += (double)pr[k] * (double)zr[k];
-      const double ld = (double)Erow[t] - x + (double)Mrow[t] * (double)lse;
+      ld = (double)Erow[t] - x + (double)Mrow[t] * (double)lse;
       l = (float)ld;
-      contrib = ld;
     }
     lse_out[t] = lse;
     if (row_loss) row_loss[t] = l;
+    row_ld[t] = ld;
   }
-  red[threadIdx.x] = contrib;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) blk_sum[blockIdx.x] = red[0];
 }
 
-__global__ __launch_bounds__(256) void loss_reduce_kernel(const double* __restrict__ blk_sum, int nblk,
+// loss = sum_t row_ld[t] / N, summed in a fixed order (one block).
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const double* __restrict__ row_ld, int T,
                                                           const int* __restrict__ N, float* __restrict__ loss) {
   __shared__ double red[256];
   double a = 0.0;
-  for (int i = threadIdx.x; i < nblk; i += 256) a += blk_sum[i];
+  for (int i = threadIdx.x; i < T; i += 256) a += row_ld[i];
   red[threadIdx.x] = a;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -500,15 +506,14 @@ __global__ __launch_bounds__(256) void fwd_shard_rows_kernel(const float2* __res
 
 // One thread per row: merge the shards' partial LSE (fp64 log-sum-exp of the
 // natural-log partials) and cross terms into LSE and l_t = E - sum cross +
-// M LSE; masked rows give 0; per-256-row fp64 sums as in fwd_finalize.
+// M LSE; masked rows give 0; l_t in fp64 at row_ld[t] as in fwd_finalize.
 __global__ __launch_bounds__(256) void shard_combine_kernel(const float* __restrict__ lse_parts,
                                                             const float* __restrict__ cross_parts, int S, int T,
                                                             const float* __restrict__ Erow,
                                                             const float* __restrict__ Mrow,
                                                             const uint8_t* __restrict__ mask,
                                                             float* __restrict__ lse_out, float* __restrict__ row_loss,
-                                                            double* __restrict__ blk_sum) {
-  __shared__ double red[256];
+                                                            double* __restrict__ row_ld) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   double contrib = 0.0;
   if (t < T) {
@@ -530,14 +535,8 @@ __global__ __launch_bounds__(256) void shard_combine_kernel(const float* __restr
     }
     lse_out[t] = lse;
     if (row_loss) row_loss[t] = l;
+    row_ld[t] = contrib;
   }
-  red[threadIdx.x] = contrib;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) blk_sum[blockIdx.x] = red[0];
 }
 
 // ----------------------------------------------------- transposes / casts --
@@ -558,6 +557,48 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict_
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
     if (c < C && r < Rp) dst[(int64_t)c * ldd + r] = tileS[tx][i];
+  }
+}
+
+// bf16, 128 x 128 tiles: 16-byte loads of the rows into LDS (the 16-byte
+// chunk c of row r at c ^ (r / 8 mod 16)), then each thread transposes one
+// 8 x 8 block in registers and writes eight 16-byte pieces of dst rows;
+// requires C % 8 == 0 and Rp % 128 == 0.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src, int R, int C, int Rp,
+                                                             bf16_t* __restrict__ dst, int64_t ldd) {
+  __shared__ __attribute__((aligned(16))) uint16_t tr[128 * 128];
+  const int r0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+  const int tid = threadIdx.x;
+  u32x4 x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = j * 256 + tid, rl = q >> 4, cc = q & 15;
+    const int r = r0 + rl, c = c0 + cc * 8;
+    x[j] = u32x4{0u, 0u, 0u, 0u};
+    if (r < R && c < C) x[j] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * C + c);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = j * 256 + tid, rl = q >> 4, cc = q & 15;
+    reinterpret_cast<u32x4*>(tr + rl * 128)[cc ^ ((rl >> 3) & 15)] = x[j];
+  }
+  __syncthreads();
+  const int rb = tid & 15, cb = tid >> 4;
+  u32x4 a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = reinterpret_cast<const u32x4*>(tr + (rb * 8 + i) * 128)[cb ^ rb];
+  if (r0 + rb * 8 >= Rp) return;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // dst rows 2w (low halves) and 2w + 1 (high halves) of the block
+    u32x4 lo, hi;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      lo[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x05040100u);
+      hi[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x07060302u);
+    }
+    const int c = c0 + cb * 8 + 2 * w;
+    if (c < C) *reinterpret_cast<u32x4*>(dst + (int64_t)c * ldd + r0 + rb * 8) = lo;
+    if (c + 1 < C) *reinterpret_cast<u32x4*>(dst + (int64_t)(c + 1) * ldd + r0 + rb * 8) = hi;
   }
 }
 
@@ -1154,26 +1195,26 @@ hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int 
 
 hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                            const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
-                           double* blk_sum, hipStream_t st) {
-  const int nblk = (T + 255) / 256;
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(256), 0, st, (const float2*)part, S, T, K, p_s, zg_s, Erow,
-                     Mrow, mask, lse, row_loss, blk_sum);
+                           double* row_ld, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3((T + 15) / 16), dim3(256), 0, st, (const float2*)part, S, T, K, p_s,
+                     zg_s, Erow, Mrow, mask, lse, row_loss, row_ld);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
-hipError_t launch_loss_reduce(const double* blk_sum, int nblk, const int* N, float* loss, hipStream_t st) {
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, blk_sum, nblk, N, loss);
+hipError_t launch_loss_reduce(const double* row_ld, int T, const int* N, float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, row_ld, T, N, loss);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
 hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
-                               float* row_loss, double* blk_sum, const int* N, float* loss, hipStream_t st) {
-  hipError_t e = launch_fwd_rows(part, S, T, K, p_s, zg_s, Erow, Mrow, mask, lse, row_loss, blk_sum, st);
+                               float* row_loss, double* row_ld, const int* N, float* loss, hipStream_t st) {
+  hipError_t e = launch_fwd_rows(part, S, T, K, p_s, zg_s, Erow, Mrow, mask, lse, row_loss, row_ld, st);
   if (e != hipSuccess) return e;
-  return launch_loss_reduce(blk_sum, (T + 255) / 256, N, loss, st);
+  return launch_loss_reduce(row_ld, T, N, loss, st);
 }
 
 hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
@@ -1185,17 +1226,23 @@ hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const fl
 }
 
 hipError_t launch_shard_combine(const float* lse_parts, const float* cross_parts, int S, int T, const float* Erow,
-                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* blk_sum,
+                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* row_ld,
                                 const int* N, float* loss, hipStream_t st) {
   const int nblk = (T + 255) / 256;
   hipLaunchKernelGGL(shard_combine_kernel, dim3(nblk), dim3(256), 0, st, lse_parts, cross_parts, S, T, Erow, Mrow,
-                     mask, lse, row_loss, blk_sum);
+                     mask, lse, row_loss, row_ld);
   CKL_LAUNCH_CHECK();
-  return launch_loss_reduce(blk_sum, nblk, N, loss, st);
+  return launch_loss_reduce(row_ld, T, N, loss, st);
 }
 
 hipError_t launch_transpose_pad(int in_bf16, const void* src, int R, int C, int Rp, void* dst, int64_t ldd,
                                 hipStream_t st) {
+  if (in_bf16 && C % 8 == 0 && Rp % 128 == 0 && ldd % 8 == 0) {
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(Rp / 128, (C + 127) / 128), dim3(256), 0, st, (const bf16_t*)src, R,
+                       C, Rp, (bf16_t*)dst, ldd);
+    CKL_LAUNCH_CHECK();
+    return hipSuccess;
+  }
   dim3 grid((Rp + 63) / 64, (C + 63) / 64);
   if (in_bf16)
     hipLaunchKernelGGL(transpose_pad_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src, R, C, Rp,

@@ -22,7 +22,7 @@ hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K
 hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                  float* lse_part, float* cross_part, hipStream_t st);
 hipError_t launch_shard_combine(const float* lse_parts, const float* cross_parts, int S, int T, const float* Erow,
-                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* blk_sum,
+                                const float* Mrow, const uint8_t* mask, float* lse, float* row_loss, double* row_ld,
                                 const int* N, float* loss, hipStream_t st);
 // G == nullptr: log-sum-exp partials only.  Otherwise also the exponentials
 // u (G, row stride ldG) and the per-tile maxima (mtab, row stride ldm) of the
@@ -33,11 +33,12 @@ hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int 
 // Per-row LSE and loss plus per-256-row fp64 sums; then the mean over N.
 hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                            const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
-                           double* blk_sum, hipStream_t st);
-hipError_t launch_loss_reduce(const double* blk_sum, int nblk, const int* N, float* loss, hipStream_t st);
+                           double* row_ld, hipStream_t st);
+// loss = sum of row_ld[0 .. T) (fp64, fixed order) / *N
+hipError_t launch_loss_reduce(const double* row_ld, int T, const int* N, float* loss, hipStream_t st);
 hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
-                               float* row_loss, double* blk_sum, const int* N, float* loss, hipStream_t st);
+                               float* row_loss, double* row_ld, const int* N, float* loss, hipStream_t st);
 // Fused path, after the rows' LSE is known: G[t][v] (holding u) becomes
 // g = s_t M_t u 2^(m - lse_t log2e) in place, zero for t >= rows, v >= V or
 // s_t = 0, and G^T[v][t] = g, over t < rows_p and v < Vp (tile multiples).
