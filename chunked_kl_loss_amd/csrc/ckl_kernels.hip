@@ -268,9 +268,10 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   }
 
   TileT tile;
-  // With the substep loop, the next tile's first two slices are issued right
-  // after a tile's k loop, so that their latency overlaps this tile's epilogue
-  // (registers and global memory only; the LDS stages are untouched).
+  // With the substep loop, the next tile's first two slices are issued at the
+  // end of a tile's epilogue (registers and global memory only; the LDS
+  // stages are untouched), after its stores: the next k loop starts by
+  // waiting for both, and the stores, issued first, are then mostly done.
   constexpr bool kAhead = PrefetchOK<C>::value;
   const TIn* Ht0 = H + (int64_t)t0 * d;
   if constexpr (kAhead)
@@ -279,8 +280,6 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     const int v0 = vt * C::BM;
     if constexpr (kAhead) {
       run_mma<C, true>(tile, W + (int64_t)v0 * d, d, V - v0, Ht0, d, T - t0, d, smem);
-      if (vt + 1 < vt1)
-        tile_k64_prologue<C>(W + (int64_t)(v0 + C::BM) * d, d, V - v0 - C::BM, Ht0, d, T - t0, d, smem);
     } else {
       run_mma(tile, W + (int64_t)v0 * d, d, V - v0, Ht0, d, T - t0, d, smem);
     }
@@ -395,6 +394,9 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
         if (own) mtab[((int64_t)vt * C::WAVES_M + wave_m) * ldm + trow] = mn;
       }
     }
+    if constexpr (kAhead)
+      if (vt + 1 < vt1)
+        tile_k64_prologue<C>(W + (int64_t)(v0 + C::BM) * d, d, V - v0 - C::BM, Ht0, d, T - t0, d, smem);
   }
 
   // merge across the WAVES_M waves sharing the same tokens (each lane owns
@@ -463,14 +465,14 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restr
 }
 
 // loss = sum_t row_ld[t] / N, summed in a fixed order (one block).
-__global__ __launch_bounds__(256) void loss_reduce_kernel(const double* __restrict__ row_ld, int T,
-                                                          const int* __restrict__ N, float* __restrict__ loss) {
-  __shared__ double red[256];
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const double* __restrict__ row_ld, int T,
+                                                           const int* __restrict__ N, float* __restrict__ loss) {
+  __shared__ double red[1024];
   double a = 0.0;
-  for (int i = threadIdx.x; i < T; i += 256) a += row_ld[i];
+  for (int i = threadIdx.x; i < T; i += 1024) a += row_ld[i];
   red[threadIdx.x] = a;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = 512; s > 0; s >>= 1) {
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
@@ -823,34 +825,40 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
 // then writes G rows and, through 8 x 8 register transposes, G^T rows, in
 // 512- and 256-byte runs.  64 KiB of LDS: two blocks per CU, one reading while
 // the other writes.  HBM traffic 3 elements per entry, in whole cache lines.
-__global__ __launch_bounds__(512) void gpass_tiles_kernel(const bf16_t* __restrict__ U, int n_vtiles,
-                                                          bf16_t* __restrict__ G, int64_t ldG, bf16_t* __restrict__ Gt,
-                                                          int64_t ldGt, const float* __restrict__ mtab, int64_t ldm,
-                                                          const float* __restrict__ srow,
-                                                          const float* __restrict__ Mrow,
-                                                          const float* __restrict__ lse, int rows, int V) {
+template <int TH>
+__global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __restrict__ U, int n_vtiles,
+                                                               bf16_t* __restrict__ G, int64_t ldG,
+                                                               bf16_t* __restrict__ Gt, int64_t ldGt,
+                                                               const float* __restrict__ mtab, int64_t ldm,
+                                                               const float* __restrict__ srow,
+                                                               const float* __restrict__ Mrow,
+                                                               const float* __restrict__ lse, int rows, int V) {
   using C = CfgBF16;
   static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128 && C::WN == 64 && C::MB == 4 && C::NB == 2 &&
                     C::WAVES_M == 2 && C::WAVES_N == 4,
                 "tile order written by fwd_lse_kernel");
-  __shared__ __attribute__((aligned(16))) uint16_t tr[128 * 256];
-  __shared__ float fs[2][128];  // g / u per (wave_m, token): s_t M_t 2^(m - LSE_t log2e), 0 for no gradient
-  const int vt = blockIdx.x, tb = blockIdx.y >> 1, th = blockIdx.y & 1;
-  const int t0 = tb * 256 + th * 128, v0 = vt * 256;
+  static_assert(TH == 1 || TH == 2, "64 or 128 tokens per block");
+  constexpr int NT = 256 * TH;    // threads
+  constexpr int TR = 64 * TH;     // token rows of the slab
+  constexpr int NCH = TR * 32;    // 16-byte chunks of the slab (and per thread: NCH / NT = 8)
+  __shared__ __attribute__((aligned(16))) uint16_t tr[TR * 256];
+  __shared__ float fs[2][TR];  // g / u per (wave_m, token): s_t M_t 2^(m - LSE_t log2e), 0 for no gradient
+  const int vt = blockIdx.x, tb = blockIdx.y / (4 / TH), th = blockIdx.y % (4 / TH);
+  const int t0 = tb * 256 + th * TR, v0 = vt * 256;
   const int tid = threadIdx.x;
   const u32x4* ut = reinterpret_cast<const u32x4*>(U + ((int64_t)tb * n_vtiles + vt) * (256 * 256));
   auto phys = [](int t, int c) { return c ^ ((t >> 3) & 31); };
-  // wave w of the forward wrote its 16 KiB (1024 chunks) at chunk 1024 w;
-  // this half holds waves 2 th, 2 th + 1 (wave_m 0) and 4 + 2 th, 5 + 2 th
+  // wave w of the forward wrote its 16 KiB (1024 chunks) at chunk 1024 w; this
+  // slab holds the waves with wave_n in [TH th, TH th + TH), for wave_m 0 and 1
   auto src_chunk = [&](int c) {
-    const int p = c >> 10;
-    return (((p & 1) + 2 * th + 4 * (p >> 1)) << 10) + (c & 1023);
+    const int p = c >> 10;  // TH pieces per wave_m
+    return (((p % TH) + TH * th + 4 * (p / TH)) << 10) + (c & 1023);
   };
   u32x4 x[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = ut[src_chunk(j * 512 + tid)];
-  if (tid < 256) {
-    const int wm = tid >> 7, tl = tid & 127, t = t0 + tl;
+  for (int j = 0; j < 8; ++j) x[j] = ut[src_chunk(j * NT + tid)];
+  if (tid < 2 * TR) {
+    const int wm = tid / TR, tl = tid % TR, t = t0 + tl;
     float f = 0.f;
     if (t < rows) {
       const float sc = srow[t];
@@ -861,10 +869,10 @@ __global__ __launch_bounds__(512) void gpass_tiles_kernel(const bf16_t* __restri
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int c = j * 512 + tid;
+    const int c = j * NT + tid;
     const int p = c >> 10, cw = c & 1023;
-    const int lane = cw & 63, h = (cw >> 6) & 1, nb = (cw >> 7) & 1, mb = (cw >> 8) & 3, wm = p >> 1;
-    const int tl = (p & 1) * 64 + nb * 32 + (lane & 31);
+    const int lane = cw & 63, h = (cw >> 6) & 1, nb = (cw >> 7) & 1, mb = (cw >> 8) & 3, wm = p / TH;
+    const int tl = (p % TH) * 64 + nb * 32 + (lane & 31);
     const int vl = wm * 128 + mb * 32 + 16 * h + 4 * (lane >> 5);  // elements 0-3: vl.., 4-7: vl + 8..
     const float f = fs[wm][tl];
     // rows past `rows` and masked rows (f = 0) may hold stale u: select,
@@ -887,14 +895,15 @@ __global__ __launch_bounds__(512) void gpass_tiles_kernel(const bf16_t* __restri
   // G rows: 32 threads per row of 256 entries
 #pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
-    const int tl = pass * 16 + (tid >> 5), q = tid & 31;
+    const int tl = pass * (NT / 32) + (tid >> 5), q = tid & 31;
     const u32x4 v = reinterpret_cast<const u32x4*>(tr + tl * 256)[phys(tl, q)];
     *reinterpret_cast<u32x4*>(G + (int64_t)(t0 + tl) * ldG + v0 + q * 8) = v;
   }
   // G^T rows: thread (tq, vb) transposes the 8 x 8 block of tokens 8 tq ..,
-  // vocabulary rows 8 vb ..; 16 threads write one 256-byte row run
+  // vocabulary rows 8 vb ..; TR / 8 threads write one row run of 2 TR bytes
   {
-    const int tq = tid & 15, vb = tid >> 4;
+    constexpr int NTQ = TR / 8;
+    const int tq = tid % NTQ, vb = tid / NTQ;
     u32x4 a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = reinterpret_cast<const u32x4*>(tr + (tq * 8 + i) * 256)[vb ^ tq];
@@ -1204,7 +1213,7 @@ hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p
 }
 
 hipError_t launch_loss_reduce(const double* row_ld, int T, const int* N, float* loss, hipStream_t st) {
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, row_ld, T, N, loss);
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, st, row_ld, T, N, loss);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -1336,12 +1345,15 @@ hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldG
   return hipSuccess;
 }
 
+constexpr int kGpassTH = 2;  // forward wave columns (64 tokens each) per G-formation block
+
 hipError_t launch_gpass_tiles(const void* U, int n_vtiles, int n_tblocks, void* G, int64_t ldG, void* Gt,
                               int64_t ldGt, const float* mtab, int64_t ldm, const float* srow, const float* Mrow,
                               const float* lse, int rows, int V, hipStream_t st) {
   if (n_vtiles < 1 || n_tblocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(gpass_tiles_kernel, dim3(n_vtiles, 2 * n_tblocks), dim3(512), 0, st, (const bf16_t*)U, n_vtiles,
-                     (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm, srow, Mrow, lse, rows, V);
+  hipLaunchKernelGGL(gpass_tiles_kernel<kGpassTH>, dim3(n_vtiles, (4 / kGpassTH) * n_tblocks), dim3(256 * kGpassTH), 0,
+                     st, (const bf16_t*)U, n_vtiles, (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm, srow, Mrow, lse,
+                     rows, V);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
