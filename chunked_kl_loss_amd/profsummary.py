@@ -19,7 +19,7 @@ import json
 import sys
 
 CLASSES = (("fwd_lse", "fwd_lse"), ("bwd_grad", "bwd_grad"), ("gemm_store", "gemm_dhdw"),
-           ("gpass", "g_pass"), ("transpose_pad", "transpose"), ("teacher_prep", "teacher_prep"),
+           ("gpass", "g_pass"), ("transpose", "transpose"), ("teacher_prep", "teacher_prep"),
            ("fwd_finalize", "fwd_finalize"), ("loss_reduce", "fwd_finalize"))
 
 
