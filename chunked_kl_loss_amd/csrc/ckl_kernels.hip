@@ -288,21 +288,31 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     if constexpr (!kAhead) wait_vmcnt<0>();
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
+    const bool full = vbase + C::WM <= V;  // every row of the wave's slice is a vocabulary row
 #pragma unroll
     for (int nb = 0; nb < NBK; ++nb) {
       const int src = (lane & (GLANES - 1)) + nb * GLANES;  // the owner of column nb
       const bool own = own_nb == nb;
       const int tok = opaque(t0 + wave_n * C::WN + nb * BLK + (lane & (BLK - 1)));
+      // (max before the scaling by log2e > 0: the same value, one multiply)
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int mb = 0; mb < MBK; ++mb)
+        for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-        for (int r = 0; r < RPB; ++r) {
-          const int v = vbase + mb * BLK + L::row_in(r, lane);
-          if (v < V) mx = fmaxf(mx, tile.acc[mb][nb][r] * kLog2e);
-        }
+          for (int r = 0; r < RPB; ++r) mx = fmaxf(mx, tile.acc[mb][nb][r]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MBK; ++mb)
+#pragma unroll
+          for (int r = 0; r < RPB; ++r) {
+            const int v = vbase + mb * BLK + L::row_in(r, lane);
+            if (v < V) mx = fmaxf(mx, tile.acc[mb][nb][r]);
+          }
+      }
 #pragma unroll
       for (int o = GLANES; o < 64; o *= 2) mx = fmaxf(mx, __shfl_xor(mx, o));
+      mx *= kLog2e;
       const float crm = __shfl(rm, src);
       const float mn = fmaxf(crm, mx);
       // logits at the teacher indices of this token that fall in this tile;
@@ -342,15 +352,26 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
       }
       float ssum = 0.f;
       if (mn != -INFINITY) {
+        if (full) {
 #pragma unroll
-        for (int mb = 0; mb < MBK; ++mb)
+          for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
-          for (int r = 0; r < RPB; ++r) {
-            const int v = vbase + mb * BLK + L::row_in(r, lane);
-            const float u = v < V ? fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn) : 0.f;
-            ssum += u;
-            if constexpr (STORE) tile.acc[mb][nb][r] = u;
-          }
+            for (int r = 0; r < RPB; ++r) {
+              const float u = fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn);
+              ssum += u;
+              if constexpr (STORE) tile.acc[mb][nb][r] = u;
+            }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MBK; ++mb)
+#pragma unroll
+            for (int r = 0; r < RPB; ++r) {
+              const int v = vbase + mb * BLK + L::row_in(r, lane);
+              const float u = v < V ? fast_exp2(tile.acc[mb][nb][r] * kLog2e - mn) : 0.f;
+              ssum += u;
+              if constexpr (STORE) tile.acc[mb][nb][r] = u;
+            }
+        }
 #pragma unroll
         for (int o = GLANES; o < 64; o *= 2) ssum += __shfl_xor(ssum, o);
         if (own) {
