@@ -1007,7 +1007,7 @@ struct GemmProblem {
   int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN) * batches
 };
 
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 2;
 
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typename C::TIn> p0,
