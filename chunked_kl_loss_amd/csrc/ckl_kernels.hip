@@ -1012,7 +1012,12 @@ constexpr int kGroupM = 2;
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typename C::TIn> p0,
                                                                  GemmProblem<typename C::TIn> p1) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  // bf16 configurations stage the fp32 output through LDS one wave row block
+  // at a time and bring the old values of the read-modify-write in beside it
+  // by global->LDS loads: two blocks of WM x BN fp32, up to 160 KiB.
+  constexpr int kOldDma = std::is_same<typename C::TIn, bf16_t>::value && 2 * C::WM * C::BN * 4 <= 160 * 1024 ? 1 : 0;
+  constexpr int kSmem = kOldDma && 2 * C::WM * C::BN * 4 > C::LDS_BYTES ? 2 * C::WM * C::BN * 4 : C::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
@@ -1069,6 +1074,63 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
     auto stage_swz = [](int ml) { return ((ml >> 2) & (L::GROUPS - 1)) * L::BLK; };
     static_assert(C::BN % (L::GROUPS * L::BLK) == 0, "the swizzle stays inside a row");
     const bool vec_ok = (ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    if constexpr (kOldDma) {
+      if (vec_ok) {
+        // Old values (dW update): the part's rows go global->LDS into the
+        // second block (chunk q = row * BN / 4 + column / 4 at 16 q bytes,
+        // 64 chunks per wave load), issued before the staging so that their
+        // latency overlaps it; one wait and barrier per part.
+        float* oldb = st + PART * C::BN;
+        constexpr int CPR = C::BN / 4;                 // 16-byte chunks per row
+        constexpr int NLD = PART * CPR / 64 / C::NWAVES;  // wave loads per part
+        static_assert(PART * CPR % (64 * C::NWAVES) == 0, "whole wave loads");
+#pragma unroll 1
+        for (int part = 0; part < C::WAVES_M; ++part) {
+          const int r0 = m0 + part * PART;
+          if (beta && r0 < M) {
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(out + (int64_t)r0 * ldo, (uint32_t)(min(M - r0, PART) * ldo * 4));
+#pragma unroll
+            for (int k = 0; k < NLD; ++k) {
+              const int q = (k * C::NWAVES + wave) * 64 + lane;
+              const int row = q / CPR, c4 = (q % CPR) * 4;
+              const bool in = n0 + c4 + 4 <= N;
+              lds_dma_buf(ro, in ? (uint32_t)((row * ldo + n0 + c4) * 4) : kOutOfRange, 0u,
+                          oldb + (k * C::NWAVES + wave) * 256);
+            }
+          }
+          if (wave_m == part) {
+#pragma unroll
+            for (int mb = 0; mb < TileT::MBK; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < TileT::NBK; ++nb) {
+                const int nl = wave_n * C::WN + nb * L::BLK + (lane & (L::BLK - 1));
+#pragma unroll
+                for (int r = 0; r < L::RPB; ++r) {
+                  const int ml = mb * L::BLK + L::row_in(r, lane);
+                  st[ml * C::BN + (nl ^ stage_swz(ml))] = tile.acc[mb][nb][r];
+                }
+              }
+          }
+          wait_vmcnt<0>();
+          __syncthreads();
+          for (int i = threadIdx.x; i < PART * CPR; i += C::NTHREADS) {
+            const int ml = i / CPR, c4 = (i % CPR) * 4;
+            const int m = r0 + ml, n = n0 + c4;
+            if (m >= M || n >= N) continue;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(st + ml * C::BN + (c4 ^ stage_swz(ml)));
+            float* o = out + (int64_t)m * ldo + n;
+            if (n + 4 <= N) {
+              *reinterpret_cast<f32x4*>(o) = beta ? a + *reinterpret_cast<const f32x4*>(oldb + i * 4) : a;
+            } else {
+              for (int e = 0; e < 4 && n + e < N; ++e) o[e] = beta ? o[e] + a[e] : a[e];
+            }
+          }
+          __syncthreads();
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int part = 0; part < C::WAVES_M; ++part) {
       if (wave_m == part) {
