@@ -11,6 +11,8 @@ max-abs 1e-2 of max|ref|; fp32 inputs: 1e-5), which the extra rounding of
 exp(z - m) to bf16 (one bf16 ulp, 2^-8 relative at most, on each non-teacher
 entry of G before it is rescaled) stays well inside.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -196,3 +198,17 @@ def test_fused_odd_chunk_count():
     say(f"case fused odd chunk count T={x.T} plan={plan}")
     got = run_gpu_fused(x, chunk=200, grad_loss=1.25)
     check_full(x, got, oracle_full(x, grad_loss=1.25), TOL["bf16"], 2e-3)
+
+
+def test_fused_clustered_teacher_indices():
+    # each row's K teacher indices are one run of consecutive vocabulary rows
+    # (wrapping at V): a logit tile holds many of a token's indices at once,
+    # so the gather walks several entries per tile, across tile boundaries
+    x = _custom(300, 64, 5000, 100)
+    rng = np.random.default_rng(11)
+    start = rng.integers(0, x.V, size=x.T)
+    idx = ((start[:, None] + np.arange(x.K)[None, :]) % x.V).astype(np.int32)
+    x = dataclasses.replace(x, idx=idx)
+    say(f"case clustered teacher indices T={x.T} V={x.V} K={x.K}")
+    got = run_gpu_fused(x, chunk=64, grad_loss=0.5)
+    check_full(x, got, oracle_full(x, grad_loss=0.5), TOL["bf16"], 2e-3)

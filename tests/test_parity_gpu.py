@@ -12,6 +12,8 @@ absolute error <= 2e-3 for bf16 (fp32 accumulation of d products of size
 ~|h||w|/d plus fp32 exponent sums; observed errors are ~1e-5) and <= 1e-5 for
 fp32.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -56,7 +58,6 @@ def with_logprob_teacher(x, seed=31, extra=400, n_neg_inf=0):
     """The same problem with the K cached values replaced by the top-K
     log-probabilities of a teacher over K + extra classes (teacher mass below
     one), optionally with some -inf entries (zero-probability tokens)."""
-    import dataclasses
     rng = np.random.default_rng(seed)
     full = rng.normal(0.0, 2.0, size=(x.T, x.K + extra))
     full -= full.max(axis=1, keepdims=True)
@@ -234,3 +235,17 @@ def test_logprob_teacher_bf16_large_vocab():
     say(f"case log-prob teacher cfg4 slice T={x.T} masked={x.mask is not None}")
     got = run_gpu(x, teacher_form=1, chunk=300)
     check_full(x, got, oracle_full(x, teacher_form=1), TOL["bf16"], 2e-3)
+
+
+def test_clustered_teacher_indices():
+    # each row's K teacher indices are one run of consecutive vocabulary rows
+    # (wrapping at V): a logit tile holds many of a token's indices at once,
+    # so the gather walks several entries per tile, across tile boundaries
+    x = _custom(300, 64, 5000, 100)
+    rng = np.random.default_rng(11)
+    start = rng.integers(0, x.V, size=x.T)
+    idx = ((start[:, None] + np.arange(x.K)[None, :]) % x.V).astype(np.int32)
+    x = dataclasses.replace(x, idx=idx)
+    say(f"case clustered teacher indices T={x.T} V={x.V} K={x.K}")
+    got = run_gpu(x, chunk=64, grad_loss=0.5)
+    check_full(x, got, oracle_full(x, grad_loss=0.5), TOL["bf16"], 2e-3)
