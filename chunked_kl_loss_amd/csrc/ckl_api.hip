@@ -50,10 +50,15 @@ constexpr int64_t kCUs = 256;
 // main loop (a 256 x 256 fp32 tile at one CU's share of HBM bandwidth).
 constexpr int64_t kMaxSplit = 64;
 constexpr int64_t kEpilogueK = 512;
-// Fused call: G^T keeps the columns of this many consecutive row chunks, so
-// the dW update (an fp32 read-modify-write of all of dW) runs once per group
-// with k = kDwChunks * chunk rows instead of once per chunk.
-constexpr int64_t kDwChunks = 4;
+// Fused call: G^T keeps the columns of up to this many consecutive row
+// chunks, so the dW update (an fp32 read-modify-write of all of dW) runs once
+// per group with k = group * chunk rows instead of once per chunk.
+constexpr int64_t kDwChunks = 8;
+// Row padding (elements) of G^T in the fused call.  Its rows are written 256
+// bytes at a time for 256 consecutive rows; some strides put those runs on few
+// memory channels (with eight 2048-row chunks, a stride of 32 KiB + 256 bytes
+// made the G formation ~1.2x slower than 32 KiB + 640 bytes).
+constexpr int64_t kGtPad = 320;
 // The backward keeps one G block, stored as G and G^T, within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
 // the contraction of block i on a second stream measured no faster: both
@@ -131,7 +136,7 @@ struct Plan {
   int64_t Tc, Vc, nT, nV;
   // fused forward + backward: row chunks of Cs rows, nS of them; forward
   // splits per chunk; dH split-k into Sh parts of Vs vocabulary columns
-  int64_t Cs, nS, c_splits, c_tps, Sh, Vs, groups;
+  int64_t Cs, nS, Gc, c_splits, c_tps, Sh, Vs, groups;
 };
 
 // Vocabulary splits of the logit kernels: each workgroup sweeps a run of
@@ -224,6 +229,7 @@ Plan make_plan(const ckl_problem* p) {
   // block sums are per 256 rows), at most the padded row count.
   q.Cs = std::min(round_up(p->chunk, 256), round_up(q.Tp, 256));
   q.nS = ceil_div(q.Tp, q.Cs);
+  q.Gc = std::min(kDwChunks, q.nS);  // chunks per dW group
   pick_splits(q.Cs / q.BN, q.Vp / q.BM, &q.c_splits, &q.c_tps);
   // dH split-k parts: the count whose tiles finish in the fewest k-steps when
   // dealt to kCUs workgroups in rounds (whole rounds: a launch that holds only
@@ -315,7 +321,7 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   // by gpass_tiles (fp32 keeps u in G itself)
   w.U = q.in_bf16 ? take((size_t)q.Cs * q.Vp * q.esz) : 0;
   w.G = take((size_t)q.Cs * (q.Vp + kLdPad) * q.esz);
-  w.Gt = take((size_t)q.Vp * (kDwChunks * q.Cs + kLdPad) * q.esz);
+  w.Gt = take((size_t)q.Vp * (q.Gc * q.Cs + kGtPad) * q.esz);
   w.mtab = take((size_t)q.groups * q.Cs * 4);
   w.dHp = take((size_t)q.Sh * q.Cs * q.d * 4);
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
@@ -558,7 +564,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   float* dHp = (float*)(b + w.dHp);
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
-  const int64_t ldG = q.Vp + kLdPad, ldGt = kDwChunks * q.Cs + kLdPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
+  const int64_t ldG = q.Vp + kLdPad, ldGt = q.Gc * q.Cs + kGtPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
 
   HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
@@ -585,9 +591,9 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     const int64_t tb0 = c * q.Cs;
     const int rows = (int)std::min(q.Cs, q.T - tb0);           // real rows of the chunk
     const int rows_p = (int)std::min(q.Cs, q.Tp - tb0);        // whole logit tiles
-    const int64_t slot = c % kDwChunks;                          // this chunk's columns of G^T
+    const int64_t slot = c % q.Gc;                               // this chunk's columns of G^T
     char* Gtc = Gt + slot * q.Cs * q.esz;
-    const bool dw_now = slot == kDwChunks - 1 || c == q.nS - 1;  // the group's last chunk
+    const bool dw_now = slot == q.Gc - 1 || c == q.nS - 1;       // the group's last chunk
     const char* Hc = (const char*)H + tb0 * q.d * q.esz;
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
