@@ -647,7 +647,18 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
     int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
     typename C::TIn* __restrict__ Gt, int64_t ldGt) {
   using TIn = typename C::TIn;
+  // bf16 256 x 256 tiles leave the kernel through the LDS (the whole tile,
+  // 128 KiB, once the main loop is done with it) as 16-byte stores that
+  // form 512-byte runs of G and G^T rows; otherwise straight from registers.
+  constexpr bool kStage = std::is_same<TIn, bf16_t>::value && C::BM == 256 && C::BN == 256 && C::WM == 128 &&
+                          C::LDS_BYTES >= 256 * 256 * 2;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
+  // 16-byte chunk c of token row t sits at c ^ (t / 8): the column reads of
+  // eight consecutive rows spread over the banks
+  auto stage_chunk = [](int t, int c) { return c ^ ((t >> 3) & 31); };
+  (void)stg;
+  (void)stage_chunk;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wave_m = wave / C::WAVES_N;
@@ -714,29 +725,79 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
         ++cur[nb];
         nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok * K + cur[nb]] : kIdxEnd;
       }
-      // G rows: four consecutive vocabulary entries per register group
-      const int64_t trow = tok - tb0;
+      if constexpr (kStage) {
+        // g of this lane's token column into the LDS tile [t][v]: registers
+        // 4i .. 4i + 3 hold vocabulary rows 8i + 4 (lane / 32) .. + 3, one
+        // 8-byte half of the 16-byte chunk (wave_m 16 + mb 4 + i)
+        const int tl = wave_n * C::WN + nb * 32 + (lane & 31);
+        uint2* row = reinterpret_cast<uint2*>(stg + tl * 256);
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int vcol = vbase - vb0 + mb * 32 + 8 * i + 4 * (lane >> 5);
-          store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
-                      tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
+          for (int i = 0; i < 4; ++i)
+            row[stage_chunk(tl, wave_m * 16 + mb * 4 + i) * 2 + (lane >> 5)] =
+                make_uint2(pack_bf16x2(tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1]),
+                           pack_bf16x2(tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]));
+      } else {
+        // G rows: four consecutive vocabulary entries per register group
+        const int64_t trow = tok - tb0;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int vcol = vbase - vb0 + mb * 32 + 8 * i + 4 * (lane >> 5);
+            store4<TIn>(G + trow * ldG + vcol, tile.acc[mb][nb][4 * i], tile.acc[mb][nb][4 * i + 1],
+                        tile.acc[mb][nb][4 * i + 2], tile.acc[mb][nb][4 * i + 3]);
+          }
+        // G^T rows: neighbouring lanes hold neighbouring tokens; swap one value
+        // so that each lane writes a pair of tokens for one vocabulary entry.
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float a0 = tile.acc[mb][nb][r], a1 = tile.acc[mb][nb][r + 1];
+            const float recv = __shfl_xor(odd ? a0 : a1, 1);
+            const int vrow = vbase - vb0 + mb * 32 + acc_row(r, lane);
+            if (!odd) store2<TIn>(Gt + (int64_t)vrow * ldGt + trow, a0, recv);
+            else store2<TIn>(Gt + (int64_t)(vrow + 1) * ldGt + trow - 1, recv, a1);
+          }
+      }
+    }
+    if constexpr (kStage) {
+      __syncthreads();
+      const int tid = threadIdx.x;
+      bf16_t* Gtile = G + (int64_t)(t0 - tb0) * ldG + (v0 - vb0);
+      bf16_t* Gttile = Gt + (int64_t)(v0 - vb0) * ldGt + (t0 - tb0);
+      // G rows: 32 threads per token row of 256 entries (512 bytes)
+#pragma unroll 4
+      for (int pass = 0; pass < 256 / (C::NTHREADS / 32); ++pass) {
+        const int tl = pass * (C::NTHREADS / 32) + (tid >> 5), q = tid & 31;
+        const u32x4 v = reinterpret_cast<const u32x4*>(stg + tl * 256)[stage_chunk(tl, q)];
+        *reinterpret_cast<u32x4*>(Gtile + (int64_t)tl * ldG + q * 8) = v;
+      }
+      // G^T rows: an 8 x 8 block (tokens 8 tq .., vocabulary 8 vb ..) per
+      // thread and pass, transposed in registers; 32 threads write one
+      // vocabulary row's 512 bytes
+#pragma unroll 1
+      for (int pass = 0; pass < 1024 / C::NTHREADS; ++pass) {
+        const int blk = pass * C::NTHREADS + tid, tq = blk & 31, vb = blk >> 5;
+        u32x4 a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = reinterpret_cast<const u32x4*>(stg + (tq * 8 + i) * 256)[vb ^ tq];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // vocabulary rows 2w (low halves) and 2w + 1 (high halves)
+          u32x4 lo, hi;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            lo[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x05040100u);
+            hi[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x07060302u);
+          }
+          *reinterpret_cast<u32x4*>(Gttile + (int64_t)(vb * 8 + 2 * w) * ldGt + tq * 8) = lo;
+          *reinterpret_cast<u32x4*>(Gttile + (int64_t)(vb * 8 + 2 * w + 1) * ldGt + tq * 8) = hi;
         }
-      // G^T rows: neighbouring lanes hold neighbouring tokens; swap one value
-      // so that each lane writes a pair of tokens for one vocabulary entry.
-      const bool odd = lane & 1;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float a0 = tile.acc[mb][nb][r], a1 = tile.acc[mb][nb][r + 1];
-          const float recv = __shfl_xor(odd ? a0 : a1, 1);
-          const int vrow = vbase - vb0 + mb * 32 + acc_row(r, lane);
-          if (!odd) store2<TIn>(Gt + (int64_t)vrow * ldGt + trow, a0, recv);
-          else store2<TIn>(Gt + (int64_t)(vrow + 1) * ldGt + trow - 1, recv, a1);
-        }
+      }
+      __syncthreads();  // the next tile's loads refill the LDS
     }
   }
 }
