@@ -54,10 +54,11 @@ constexpr int64_t kEpilogueK = 512;
 // chunks, so the dW update (an fp32 read-modify-write of all of dW) runs once
 // per group with k = group * chunk rows instead of once per chunk.
 constexpr int64_t kDwChunks = 8;
-// Row padding (elements) of G^T in the fused call.  Its rows are written 256
-// bytes at a time for 256 consecutive rows; some strides put those runs on few
-// memory channels (with eight 2048-row chunks, a stride of 32 KiB + 256 bytes
-// made the G formation ~1.2x slower than 32 KiB + 640 bytes).
+// Row padding (elements) of G^T in the fused call (fp32; bf16 keeps no G^T).
+// Its rows are written in short runs for consecutive rows; some strides put
+// those runs on few memory channels (with eight 2048-row chunks of bf16, a
+// stride of 32 KiB + 256 bytes made the G formation ~1.2x slower than
+// 32 KiB + 640 bytes).
 constexpr int64_t kGtPad = 320;
 // The backward keeps one G block, stored as G and G^T, within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
@@ -320,8 +321,10 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   // bf16: u of a chunk in the forward's tile order, laid out as G and G^T
   // by gpass_tiles (fp32 keeps u in G itself)
   w.U = q.in_bf16 ? take((size_t)q.Cs * q.Vp * q.esz) : 0;
-  w.G = take((size_t)q.Cs * (q.Vp + kLdPad) * q.esz);
-  w.Gt = take((size_t)q.Vp * (q.Gc * q.Cs + kGtPad) * q.esz);
+  // bf16: G of the group's chunks, read k-major by the dW update (no G^T);
+  // fp32: G of one chunk and G^T of the group's chunks
+  w.G = take((size_t)(q.in_bf16 ? q.Gc : 1) * q.Cs * (q.Vp + kLdPad) * q.esz);
+  w.Gt = q.in_bf16 ? 0 : take((size_t)q.Vp * (q.Gc * q.Cs + kGtPad) * q.esz);
   w.mtab = take((size_t)q.groups * q.Cs * 4);
   w.dHp = take((size_t)q.Sh * q.Cs * q.d * 4);
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
@@ -559,7 +562,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   char* Wt = b + w.Wt;
   char* U = b + w.U;
   char* G = b + w.G;
-  char* Gt = b + w.Gt;
+  char* Gt = q.in_bf16 ? nullptr : b + w.Gt;
   float* mtab = (float*)(b + w.mtab);
   float* dHp = (float*)(b + w.dHp);
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
@@ -592,7 +595,9 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     const int rows = (int)std::min(q.Cs, q.T - tb0);           // real rows of the chunk
     const int rows_p = (int)std::min(q.Cs, q.Tp - tb0);        // whole logit tiles
     const int64_t slot = c % q.Gc;                               // this chunk's columns of G^T
-    char* Gtc = Gt + slot * q.Cs * q.esz;
+    // this chunk's rows of G (bf16) or columns of G^T (fp32)
+    char* Gc = q.in_bf16 ? G + slot * q.Cs * ldG * q.esz : G;
+    char* Gtc = q.in_bf16 ? nullptr : Gt + slot * q.Cs * q.esz;
     const bool dw_now = slot == q.Gc - 1 || c == q.nS - 1;       // the group's last chunk
     const char* Hc = (const char*)H + tb0 * q.d * q.esz;
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
@@ -612,7 +617,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
                   [&] {
                     if (q.in_bf16)
-                      return ckl::launch_gpass_tiles(U, (int)(q.Vp / q.BM), rows_p / (int)q.BN, G, ldG, Gtc, ldGt,
+                      return ckl::launch_gpass_tiles(U, (int)(q.Vp / q.BM), rows_p / (int)q.BN, Gc, ldG, Gtc, ldGt,
                                                      mtab, q.Cs, srow + tb0, M + tb0, lse + tb0, rows, V, st);
                     return ckl::launch_gpass(q.in_bf16, G, ldG, Gtc, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
                                              rows, rows_p, V, (int)q.Vp, st);
@@ -621,20 +626,23 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,
                   [&] {
                     return ckl::launch_gfix(q.in_bf16, rows, K, V, idx_s + tb0 * K, p_s + tb0 * K, zg_s + tb0 * K,
-                                            srow + tb0, M + tb0, lse + tb0, G, ldG, Gtc, ldGt, st);
+                                            srow + tb0, M + tb0, lse + tb0, Gc, ldG, Gtc, ldGt, st);
                   }),
             "gfix");
     // dH rows of the chunk as Sh split-k partials (long k: scheduled first);
     // at the group's last chunk also dW (+)= G^T H over the group's rows
-    ckl::GemmArgs gdh{G, ldG, Wt, ldW, dHp, q.d, rows, d, (int)q.Vs, 0};
+    ckl::GemmArgs gdh{Gc, ldG, Wt, ldW, dHp, q.d, rows, d, (int)q.Vs, 0};
     gdh.batches = (int)q.Sh;
     gdh.kdim_last = (int)(q.Vp - (q.Sh - 1) * q.Vs);
     gdh.xb = q.Vs;
     gdh.yb = q.Vs;
     gdh.ob = q.Cs * q.d;
     const int64_t g0 = c - slot;  // first chunk of the group
-    const ckl::GemmArgs gdw{Gt, ldGt, Ht + g0 * q.Cs * q.esz, ldH, dWacc, q.d, dw_now ? V : 0, d,
-                            (int)(slot * q.Cs + rows_p), g0 > 0};
+    // dW (+)= G^T H over the group's rows: bf16 reads G itself k-major
+    // (element (v, t) at G[t ldG + v]), fp32 reads G^T
+    ckl::GemmArgs gdw{q.in_bf16 ? (void*)G : (void*)Gt, q.in_bf16 ? ldG : ldGt, Ht + g0 * q.Cs * q.esz, ldH,
+                      dWacc, q.d, dw_now ? V : 0, d, (int)(slot * q.Cs + rows_p), g0 > 0};
+    gdw.xt = q.in_bf16;
     HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdh, gdw, st); }),
             "gemm dH parts + dW");
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,

@@ -905,8 +905,10 @@ __global__ __launch_bounds__(256) void gpass_kernel(TIn* __restrict__ G, int64_t
 // stages it in LDS as [t][v] (rows of 512 bytes; the 16-byte chunk c of row t
 // sits at c ^ (t / 8), so that eight-row column reads spread over the banks),
 // then writes G rows and, through 8 x 8 register transposes, G^T rows, in
-// 512- and 256-byte runs.  64 KiB of LDS: two blocks per CU, one reading while
-// the other writes.  HBM traffic 3 elements per entry, in whole cache lines.
+// 512- and 256-byte runs (G^T only when Gt is not null: the dW contraction
+// can read G itself k-major).  64 KiB of LDS: two blocks per CU, one reading
+// while the other writes.  HBM traffic 3 elements per entry (2 without G^T),
+// in whole cache lines.
 template <int TH>
 __global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __restrict__ U, int n_vtiles,
                                                                bf16_t* __restrict__ G, int64_t ldG,
@@ -981,9 +983,10 @@ __global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __r
     const u32x4 v = reinterpret_cast<const u32x4*>(tr + tl * 256)[phys(tl, q)];
     *reinterpret_cast<u32x4*>(G + (int64_t)(t0 + tl) * ldG + v0 + q * 8) = v;
   }
-  // G^T rows: thread (tq, vb) transposes the 8 x 8 block of tokens 8 tq ..,
-  // vocabulary rows 8 vb ..; TR / 8 threads write one row run of 2 TR bytes
-  {
+  // G^T rows (when asked for): thread (tq, vb) transposes the 8 x 8 block of
+  // tokens 8 tq .., vocabulary rows 8 vb ..; TR / 8 threads write one row run
+  // of 2 TR bytes
+  if (Gt != nullptr) {
     constexpr int NTQ = TR / 8;
     const int tq = tid % NTQ, vb = tid / NTQ;
     u32x4 a[8];
@@ -1004,7 +1007,8 @@ __global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __r
 }
 
 // Teacher columns: g = s_t (M_t 2^(zg log2e - LSE_t log2e) - p), the same
-// fp32 expression the recomputing backward evaluates, rounded once.
+// fp32 expression the recomputing backward evaluates, rounded once (into G,
+// and into G^T when Gt is not null).
 template <typename TIn>
 __global__ __launch_bounds__(256) void gfix_kernel(int rows, int K, int V, const int* __restrict__ idx_s,
                                                    const float* __restrict__ p_s, const float* __restrict__ zg_s,
@@ -1023,10 +1027,10 @@ __global__ __launch_bounds__(256) void gfix_kernel(int rows, int K, int V, const
   if constexpr (sizeof(TIn) == 2) {
     const uint16_t b = (uint16_t)f32_to_bf16_bits(g);
     reinterpret_cast<uint16_t*>(G)[(int64_t)t * ldG + v] = b;
-    reinterpret_cast<uint16_t*>(Gt)[(int64_t)v * ldGt + t] = b;
+    if (Gt != nullptr) reinterpret_cast<uint16_t*>(Gt)[(int64_t)v * ldGt + t] = b;
   } else {
     G[(int64_t)t * ldG + v] = g;
-    Gt[(int64_t)v * ldGt + t] = g;
+    if (Gt != nullptr) Gt[(int64_t)v * ldGt + t] = g;
   }
 }
 
@@ -1065,10 +1069,17 @@ struct GemmProblem {
   int M, N, kdim, beta;
   int batches, kdim_last;
   int64_t xb, yb, ob;
+  int xt;              // X k-major (Dma64 configurations with the substep pipeline)
   int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN) * batches
 };
 
 constexpr int kGroupM = 2;
+
+// Configurations whose main loop can take X k-major.
+template <class C>
+constexpr bool kXtOK = false;
+template <int BM, int BN, int WM, int WN>
+constexpr bool kXtOK<Dma64Cfg<BM, BN, WM, WN, 2, 1>> = BM % 128 == 0;
 
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typename C::TIn> p0,
@@ -1120,7 +1131,14 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
   using TileT = typename C::TileT;
   using L = typename TileT::L;
   TileT tile;
-  run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+  if constexpr (kXtOK<C>) {
+    if (second ? p1.xt : p0.xt)
+      run_mma<C, false, true>(tile, X + m0, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+    else
+      run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+  } else {
+    run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+  }
   if constexpr (C::WM * C::BN * 4 <= C::LDS_BYTES) {
     // The fp32 tile goes out through LDS, the WM rows of one wave_m at a
     // time, so that each thread reads / writes 16 contiguous bytes of an
@@ -1460,6 +1478,8 @@ static hipError_t gemm_pair_t(const GemmArgs& a0, const GemmArgs& a1, hipStream_
     p[i].xb = a[i]->xb;
     p[i].yb = a[i]->yb;
     p[i].ob = a[i]->ob;
+    p[i].xt = a[i]->xt;
+    if (a[i]->xt && (!kXtOK<C> || a[i]->batches > 1)) return hipErrorInvalidValue;
     p[i].tiles_m = a[i]->M > 0 ? (a[i]->M + C::BM - 1) / C::BM : 0;
     p[i].tiles = a[i]->M > 0 && a[i]->N > 0 ? p[i].tiles_m * ((a[i]->N + C::BN - 1) / C::BN) * p[i].batches : 0;
   }

@@ -80,6 +80,9 @@ struct GemmArgs {
   int M, N, kdim, beta;
   int batches = 1, kdim_last = 0;
   int64_t xb = 0, yb = 0, ob = 0;
+  // X stored k-major: element (m, k) at X[k ldx + m] (bf16 only; the
+  // buffer must hold whole 256-column tiles along m)
+  int xt = 0;
 };
 // Two independent products in one launch (problem 0's tiles are scheduled first).
 hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1, hipStream_t st);

@@ -334,11 +334,22 @@ struct Dma64Cfg {
 // end re-read row 0).  Lane -> (row within its 8-row group, slot); the rows
 // of load i are (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for
 // every i since NWAVES is even.
-template <class C>
+//
+// XT (BUF only): X is stored k-major, element (m, k) at X[k ldx + m] (X
+// points at the tile's first column).  A stage's X part then holds 64 k rows
+// of BM columns; slot s = (i NWAVES + wave) 64 + lane of load i takes k row
+// s / (BM / 8), 16-byte chunk (s % (BM / 8)) ^ 4 (k % 4), so that the
+// transposing fragment reads below touch distinct banks.  Each slice gets a
+// buffer resource of its own, based at its first k row and bounded by the
+// rows below kdim (so operands larger than 4 GiB work).
+template <class C, bool XT = false>
 struct K64Loader {
+  static_assert(!XT || (C::BUF && C::BM % 128 == 0), "k-major X: buffer loads, >= 16 chunks per k row");
   const bf16_t* X;
   const bf16_t* Y;
   __amdgpu_buffer_rsrc_t rx, ry;  // (unused, and dropped by the compiler, when BUF = 0)
+  int64_t ldx_;
+  uint32_t xoff[XT ? C::X_LOADS : 1];
   // BUF: byte offsets of this lane's first X and Y loads; load i adds i steps
   // (the steps are workgroup-uniform).  Otherwise element offsets of every load.
   uint32_t off[C::BUF ? 2 : C::LOADS_PER_STAGE];
@@ -350,6 +361,7 @@ struct K64Loader {
         Y(Y_),
         rx(make_rsrc(X_, (uint32_t)(min(xrows, C::BM) * ldx * 2))),
         ry(make_rsrc(Y_, (uint32_t)(min(yrows, C::BN) * ldy * 2))),
+        ldx_(ldx),
         xstep((uint32_t)(C::NWAVES * 8 * ldx * 2)),
         ystep((uint32_t)(C::NWAVES * 8 * ldy * 2)),
         kdim(kdim_) {
@@ -357,6 +369,14 @@ struct K64Loader {
     wave = wave_id();
     const int lrow = lane >> 3;
     lchunk = (lane & 7) ^ ((((wave & 1) << 2) | (lrow >> 1)) & 7);
+    if constexpr (XT) {
+      constexpr int XCH = C::BM / 8;
+#pragma unroll
+      for (int i = 0; i < C::X_LOADS; ++i) {
+        const int sl = (i * C::NWAVES + wave) * 64 + lane, k = sl / XCH, pc = sl % XCH;
+        xoff[i] = (uint32_t)(k * ldx * 2 + ((pc ^ (4 * (k & 3))) * 16));
+      }
+    }
     if constexpr (C::BUF) {
       off[0] = (uint32_t)((wave * 8 + lrow) * ldx * 2 + lchunk * 16);
       off[1] = (uint32_t)((wave * 8 + lrow) * ldy * 2 + lchunk * 16);
@@ -382,6 +402,14 @@ struct K64Loader {
   // kdim load zeros: an offset past every record (buffer loads) or the zero
   // block.
   __device__ __forceinline__ void dma(char* smem, int kt, int i, bool whole) const {
+    if constexpr (XT) {
+      if (i < C::X_LOADS) {
+        const int rows = min(C::BK, kdim - kt * C::BK);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(X + (int64_t)kt * C::BK * ldx_, (uint32_t)(rows * ldx_ * 2));
+        lds_dma_buf(r, xoff[i], 0u, lds_at(smem, kt, i));
+        return;
+      }
+    }
     const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
     if constexpr (C::BUF) {
       // the offset is formed here rather than kept per load in registers
@@ -422,12 +450,19 @@ __device__ __forceinline__ void tile_k64_prologue(const bf16_t* __restrict__ X, 
 // may be reused.  PRE (PIPE = 2 only): the prologue was issued by
 // tile_k64_prologue with the same arguments; the loop starts by waiting for
 // every outstanding vector memory operation (stores count on this GPU).
-template <class C, bool PRE = false>
+//
+// XT: X stored k-major (see K64Loader); its fragments are read with
+// ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column of
+// the 4 x 16 block whose rows the group's lanes address (lane 4 r + c gives
+// row r, columns 4 c .. 4 c + 3): two such reads (k rows 0-3, 4-7 of the
+// lane's half) make the lane's eight k values of its m row.
+template <class C, bool PRE = false, bool XT = false>
 __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __restrict__ X, int64_t ldx, int xrows,
                                              const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
                                              char* smem) {
   static_assert(C::BK == 64 && C::NSTAGE == 2, "two 64-wide stages");
   static_assert(!PRE || C::PIPE == 2, "prologue issued ahead only for the substep pipeline");
+  static_assert(!XT || (C::PIPE == 2 && !PRE), "k-major X: substep pipeline, prologue issued here");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -441,7 +476,7 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
 
-  const K64Loader<C> ld(X, ldx, xrows, Y, ldy, yrows, kdim);
+  const K64Loader<C, XT> ld(X, ldx, xrows, Y, ldy, yrows, kdim);
   const int lchunk = ld.lchunk;
   (void)lchunk;
   auto dma = [&](int kt, int i, bool whole) { ld.dma(smem, kt, i, whole); };
@@ -520,11 +555,34 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
     // substep of stage kt every wave has finished reading it: after the wait
     // for slice kt + 1 and the barrier, stage kt is refilled with slice kt + 2.
     using SF = SubFrags<C>;
+    // XT: this lane's byte offsets of its first transposing read per m block
+    // (group g = lane / 16 reads k rows 8 (g / 2) + 4 h + r, columns
+    // 16 (g % 2) + 4 c .. of its 32-block, chunk-swizzled as stored)
+    constexpr int XROW = C::BM * 2;
+    int xr[XT ? C::MB : 1];
+    if constexpr (XT) {
+      const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const int mc = wave_m * (C::WM / 8) + mb * 4 + (g & 1) * 2 + (c >> 1);
+        xr[mb] = ((g >> 1) * 8 + r) * XROW + ((mc ^ (4 * r)) * 16) + (c & 1) * 8;
+      }
+    }
     auto sread = [&](int kt, int sub, SF& f, int w) {
       const char* st = smem + (kt & 1) * C::STAGE_BYTES;
-      if (w < C::MB)
-        f.a[w] = *reinterpret_cast<const bf16x8*>(st + xwave + w * 32 * C::ROW_BYTES + roff[sub]);
-      else
+      if (w < C::MB) {
+        if constexpr (XT) {
+          typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+          const char* p = st + sub * 16 * XROW + xr[w];
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(__attribute__((address_space(3))) char*)(p + 4 * XROW));
+          f.a[w] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          f.a[w] = *reinterpret_cast<const bf16x8*>(st + xwave + w * 32 * C::ROW_BYTES + roff[sub]);
+        }
+      } else
         f.b[w - C::MB] =
             *reinterpret_cast<const bf16x8*>(st + ywave + (w - C::MB) * 32 * C::ROW_BYTES + roff[sub]);
     };
@@ -700,10 +758,10 @@ __device__ __forceinline__ void run_mma(Tile<C>& t, const typename C::TIn* X, in
                                         const typename C::TIn* Y, int64_t ldy, int yrows, int kdim, char* smem) {
   tile_mma<C>(t, X, ldx, xrows, Y, ldy, yrows, kdim, reinterpret_cast<typename C::TIn*>(smem));
 }
-template <class C, bool PRE = false>
+template <class C, bool PRE = false, bool XT = false>
 __device__ __forceinline__ void run_mma(DmaTile<C>& t, const bf16_t* X, int64_t ldx, int xrows, const bf16_t* Y,
                                         int64_t ldy, int yrows, int kdim, char* smem) {
-  tile_mma_k64<C, PRE>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
+  tile_mma_k64<C, PRE, XT>(t, X, ldx, xrows, Y, ldy, yrows, kdim, smem);
 }
 
 }  // namespace ckl
