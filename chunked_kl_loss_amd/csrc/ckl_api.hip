@@ -289,9 +289,10 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   w.bad = take(4);
   w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
   w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
+  // bf16 keeps G only (the dW contraction reads it k-major); fp32 also G^T
   for (int i = 0; i < kGBuffers; ++i) {
     w.G[i] = take((size_t)q.Tc * (q.Vc + kLdPad) * q.esz);
-    w.Gt[i] = take((size_t)q.Vc * (q.Tc + kLdPad) * q.esz);
+    w.Gt[i] = q.in_bf16 ? 0 : take((size_t)q.Vc * (q.Tc + kLdPad) * q.esz);
   }
   w.dH = p->dh_dtype == CKL_BF16 ? take((size_t)q.T * q.d * 4) : 0;
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
@@ -462,7 +463,7 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   void* Gtbuf[kGBuffers];
   for (int i = 0; i < kGBuffers; ++i) {
     Gbuf[i] = b + w.G[i];
-    Gtbuf[i] = b + w.Gt[i];
+    Gtbuf[i] = q.in_bf16 ? nullptr : b + w.Gt[i];
   }
   float* dHacc = p->dh_dtype == CKL_BF16 ? (float*)(b + w.dH) : (float*)dH;
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
@@ -510,8 +511,10 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
               "bwd_grad");
       // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)  (longer k: scheduled first)
       // dH[tb0 .. tb0 + trows) (+)= G W[vb0 .. vb0 + vrows)
-      const ckl::GemmArgs gdw{Gt, trows + kLdPad, Htb + tb0 * q.esz, q.Tp + kLdPad, dWacc + vb0 * q.d, q.d,
-                              (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
+      // (bf16: G itself, k-major: element (v, t) at G[t ldG + v]; fp32: G^T)
+      ckl::GemmArgs gdw{q.in_bf16 ? G : Gt, q.in_bf16 ? vrows + kLdPad : trows + kLdPad, Htb + tb0 * q.esz,
+                        q.Tp + kLdPad, dWacc + vb0 * q.d, q.d, (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
+      gdw.xt = q.in_bf16;
       const ckl::GemmArgs gdh{G, vrows + kLdPad, Wtb + vb0 * q.esz, q.Vp + kLdPad, dHacc + tb0 * q.d, q.d,
                               (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
       HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdw, gdh, st); }),

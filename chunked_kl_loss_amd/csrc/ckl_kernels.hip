@@ -639,6 +639,7 @@ __global__ void cast_f32_bf16_kernel(const float* __restrict__ src, bf16_t* __re
 // and writes
 //   G [t - tb0][v - vb0]  (row stride ldG)  and  Gt[v - vb0][t - tb0] (ldGt)
 // with G = s_t (M_t q_t[v] - p~_t[v]); rows t >= T and columns v >= V get 0.
+// bf16 may pass Gt = null: G alone is written.
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
@@ -776,11 +777,11 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
         const u32x4 v = reinterpret_cast<const u32x4*>(stg + tl * 256)[stage_chunk(tl, q)];
         *reinterpret_cast<u32x4*>(Gtile + (int64_t)tl * ldG + q * 8) = v;
       }
-      // G^T rows: an 8 x 8 block (tokens 8 tq .., vocabulary 8 vb ..) per
-      // thread and pass, transposed in registers; 32 threads write one
-      // vocabulary row's 512 bytes
+      // G^T rows (when asked for): an 8 x 8 block (tokens 8 tq .., vocabulary
+      // 8 vb ..) per thread and pass, transposed in registers; 32 threads
+      // write one vocabulary row's 512 bytes
 #pragma unroll 1
-      for (int pass = 0; pass < 1024 / C::NTHREADS; ++pass) {
+      for (int pass = 0; pass < (Gt != nullptr ? 1024 / C::NTHREADS : 0); ++pass) {
         const int blk = pass * C::NTHREADS + tid, tq = blk & 31, vb = blk >> 5;
         u32x4 a[8];
 #pragma unroll
