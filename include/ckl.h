@@ -145,8 +145,9 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
 /* The G-block plan ckl_backward uses for problem *p: out[0] = Tc (token rows
  * per block), out[1] = Vc (vocabulary columns per block), out[2] = number of
  * token blocks, out[3] = number of vocabulary blocks, out[4] = number of G
- * blocks held at once (each stored as G [Tc, Vc] and its transpose; all of
- * them together within about chunk * V elements).  dW is read-modified-
+ * blocks held at once (each stored as G [Tc, Vc], and for fp32 also its
+ * transpose; the two layouts' budget together is about chunk * V
+ * elements).  dW is read-modified-
  * written once per extra token block and dH once per extra vocabulary block.
  * Host-only; touches no device. */
 ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
@@ -232,7 +233,7 @@ typedef enum {
   CKL_KERNEL_FWD_FINALIZE = 2, /* split merge, row loss, masked mean          */
   CKL_KERNEL_BWD_GRAD = 3,     /* backward logit recompute + G epilogue       */
   CKL_KERNEL_GEMM_DHDW = 4,    /* dW (+)= G^T H and dH (+)= G W, one launch   */
-  CKL_KERNEL_G_PASS = 5,       /* fused call: u -> G in place, G^T          */
+  CKL_KERNEL_G_PASS = 5,       /* fused call: u -> G (fp32 also G^T)        */
   CKL_KERNEL_TRANSPOSE = 6,    /* H^T and W^T staging                         */
   CKL_KERNEL_OTHER = 7,        /* counts, scales, fills, casts               */
   CKL_KERNEL_CLASSES = 8
