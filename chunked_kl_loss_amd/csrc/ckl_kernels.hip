@@ -26,13 +26,13 @@ namespace ckl {
 
 // ----------------------------------------------------------- configurations --
 // bf16: 256 x 256 tiles on 64-wide k slices, 8 waves (2 per SIMD, so one
-// wave's loads, barriers and epilogue overlap the other's MFMAs).  The fused
-// logit kernels pipeline fragment reads per k16 substep, keeping for their
-// epilogue state the registers the plain dH / dW contraction spends on
-// fragments double-buffered per half stage.  fp32 (small problems):
-// 128 x 128 tiles, register-staged loads.
+// wave's loads, barriers and epilogue overlap the other's MFMAs), fragment
+// reads pipelined per k16 substep; the logit kernels (forward and the
+// recomputing backward) take 128 x 64 per wave, the dH / dW contraction
+// 256 x 320 tiles of 64 x 160.  fp32 (small problems): 128 x 128 tiles,
+// register-staged loads.
 using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
-using CfgBF16Bwd = Dma64Cfg<256, 256, 128, 64, 0, 0>;
+using CfgBF16Bwd = CfgBF16;
 using CfgBF16Gemm = Dma64Cfg<256, 320, 64, 160, 2>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
