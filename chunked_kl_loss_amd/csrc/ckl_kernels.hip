@@ -31,9 +31,9 @@ namespace ckl {
 // recomputing backward) take 128 x 64 per wave, the dH / dW contraction
 // 256 x 320 tiles of 64 x 160.  fp32 (small problems): 128 x 128 tiles,
 // register-staged loads.
-using CfgBF16 = Dma64Cfg<256, 256, 128, 64, 2>;
+using CfgBF16 = Dma64Cfg<256, 256, 128, 64>;
 using CfgBF16Bwd = CfgBF16;
-using CfgBF16Gemm = Dma64Cfg<256, 320, 64, 160, 2>;
+using CfgBF16Gemm = Dma64Cfg<256, 320, 64, 160>;
 using CfgF32 = TileCfg<float, 128, 128, 64, 64>;
 
 // ---------------------------------------------------------------- helpers --
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
       bf16_t* Gtile = G + (int64_t)(t0 - tb0) * ldG + (v0 - vb0);
       bf16_t* Gttile = Gt + (int64_t)(v0 - vb0) * ldGt + (t0 - tb0);
       // G rows: 32 threads per token row of 256 entries (512 bytes)
-#pragma unroll 4
+#pragma unroll 2
       for (int pass = 0; pass < 256 / (C::NTHREADS / 32); ++pass) {
         const int tl = pass * (C::NTHREADS / 32) + (tid >> 5), q = tid & 31;
         const u32x4 v = reinterpret_cast<const u32x4*>(stg + tl * 256)[stage_chunk(tl, q)];
@@ -804,8 +804,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
 }
 
 // ------------------------------------------------ fused G formation (gpass) --
-// The fused forward + backward keeps u = 2^(z log2e - m) of every logit of a
-// row chunk in G (see fwd_lse_kernel).  Once the chunk's LSE is known, one
+// fp32: the fused forward + backward keeps u = 2^(z log2e - m) of every logit
+// of a row chunk in G (see fwd_lse_kernel).  Once the chunk's LSE is known, one
 // 128 x 128 (token x vocabulary) tile per block turns u into
 //   g = s_t M_t u 2^(m - LSE_t log2e)  ( = s_t M_t exp(z - LSE_t) )
 // in place and writes the transpose G^T through LDS; HBM traffic 3 elements
@@ -1080,7 +1080,7 @@ constexpr int kGroupM = 2;
 template <class C>
 constexpr bool kXtOK = false;
 template <int BM, int BN, int WM, int WN>
-constexpr bool kXtOK<Dma64Cfg<BM, BN, WM, WN, 2, 1>> = BM % 128 == 0;
+constexpr bool kXtOK<Dma64Cfg<BM, BN, WM, WN>> = BM % 128 == 0;
 
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typename C::TIn> p0,
@@ -1498,14 +1498,11 @@ hipError_t launch_gemm_pair(int in_bf16, const GemmArgs& a0, const GemmArgs& a1,
 hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldGt, const float* mtab, int64_t ldm,
                         const float* srow, const float* Mrow, const float* lse, int rows, int rows_p, int V, int Vp,
                         hipStream_t st) {
-  if (rows_p % 128 || Vp % 128) return hipErrorInvalidValue;
+  // (bf16 takes launch_gpass_tiles: the forward keeps its u in tile order)
+  if (in_bf16 || rows_p % 128 || Vp % 128) return hipErrorInvalidValue;
   const dim3 grid(Vp / 128, rows_p / 128);
-  if (in_bf16)
-    hipLaunchKernelGGL(gpass_kernel<bf16_t>, grid, dim3(256), 0, st, (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm,
-                       srow, Mrow, lse, rows, V, CfgBF16::BM, CfgBF16::WM);
-  else
-    hipLaunchKernelGGL(gpass_kernel<float>, grid, dim3(256), 0, st, (float*)G, ldG, (float*)Gt, ldGt, mtab, ldm, srow,
-                       Mrow, lse, rows, V, CfgF32::BM, CfgF32::WM);
+  hipLaunchKernelGGL(gpass_kernel<float>, grid, dim3(256), 0, st, (float*)G, ldG, (float*)Gt, ldGt, mtab, ldm, srow,
+                     Mrow, lse, rows, V, CfgF32::BM, CfgF32::WM);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }

@@ -213,13 +213,6 @@ __device__ __forceinline__ void tile_mma(Tile<C>& tile, const typename C::TIn* _
 // ---------------------------------------------------------------------------
 // Direct global->LDS load helpers of the bf16 main loop.
 // ---------------------------------------------------------------------------
-// A 16-byte zero block: the per-lane address of a load whose k range lies
-// past the end of the operand.
-__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
-
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
 // global_load_lds_dword: 4 bytes per lane into LDS at `lds` + 4 * lane
 // (`lds` wave-uniform).
 __device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
@@ -263,12 +256,7 @@ __device__ __forceinline__ void phase_barrier() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// MFMA operand fragments read from LDS: two k16 substeps (Frags) or one
-// (SubFrags).
-template <class C>
-struct Frags {
-  bf16x8 a[2][C::MB], b[2][C::NB];
-};
+// MFMA operand fragments of one k16 substep, read from LDS.
 template <class C>
 struct SubFrags {
   bf16x8 a[C::MB], b[C::NB];
@@ -285,30 +273,18 @@ struct SubFrags {
 // lanes of a ds_read_b128 quarter-wave (sixteen consecutive rows, one chunk)
 // then fall in sixteen distinct 16-byte bank groups.
 //
-// Two stages fill 128 KiB, so the pipeline runs on half stages: half-step h
-// multiplies k16 substeps 2 (h & 1) and 2 (h & 1) + 1 of stage h >> 1 from
-// registers while the LDS fragments of half-step h + 1 are read.  At the
-// start of each odd half-step every wave has read all of its stage (LDS
-// counter drained, then a barrier), and this thread's loads of the next
-// stage are complete (vmcnt 0): after the barrier the stage just finished is
-// refilled with slice s + 2, its loads spread over that half-step's MFMAs.
+// The pipeline runs per k16 substep: the MFMAs of substep q use fragments
+// read under the MFMAs of substep q - 1 (two fragment sets of one substep
+// each).  At the last substep of stage kt every wave has finished reading it:
+// after the wait for slice kt + 1 and a barrier, stage kt is refilled with
+// slice kt + 2, its loads spread over that substep's MFMAs.  Operands go
+// global->LDS with buffer_load ... lds (see K64Loader).
 // ---------------------------------------------------------------------------
-//
-// PIPE = 0 drops the register double-buffering of the fragments (for kernels
-// whose epilogue state leaves no room for it): each stage is then read and
-// multiplied one k16 substep at a time, and the finished stage is refilled
-// right after the barrier that starts the next one.  PIPE = 2 pipelines at
-// substep granularity (two fragment sets of one substep each).
-//
-// BUF = 0 issues global_load_lds with per-lane 64-bit addresses (rows past the
-// end re-read row 0, chunks past kdim read a zero block) instead of buffer
-// loads; it needs fewer scalar registers, which the recomputing backward's
-// epilogue wants.
-template <int BM_, int BN_, int WM_, int WN_, int PIPE_ = 1, int BUF_ = 1>
+template <int BM_, int BN_, int WM_, int WN_>
 struct Dma64Cfg {
   using TIn = bf16_t;
   using TileT = DmaTile<Dma64Cfg>;
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 2, PIPE = PIPE_, BUF = BUF_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 2;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NTHREADS = 64 * NWAVES;
@@ -326,16 +302,15 @@ struct Dma64Cfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// Operand loader of the 64-wide loop.  With BUF: buffer_load ... lds through
-// one buffer resource per operand, based at the tile's first row and bounded
-// by its valid rows, so rows past xrows / yrows read as zero without a clamp;
+// Operand loader of the 64-wide loop: buffer_load ... lds through one buffer
+// resource per operand, based at the tile's first row and bounded by its
+// valid rows, so rows past xrows / yrows read as zero without a clamp;
 // per-lane byte offsets stay fixed and the k slice advances in the scalar
-// offset.  Without BUF: global_load_lds with element offsets (rows past the
-// end re-read row 0).  Lane -> (row within its 8-row group, slot); the rows
-// of load i are (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for
-// every i since NWAVES is even.
+// offset.  Lane -> (row within its 8-row group, slot); the rows of load i are
+// (wave + i NWAVES) 8 + lrow, whose (r >> 1) & 7 is the same for every i since
+// NWAVES is even.
 //
-// XT (BUF only): X is stored k-major, element (m, k) at X[k ldx + m] (X
+// XT: X is stored k-major, element (m, k) at X[k ldx + m] (X
 // points at the tile's first column).  A stage's X part then holds 64 k rows
 // of BM columns; slot s = (i NWAVES + wave) 64 + lane of load i takes k row
 // s / (BM / 8), 16-byte chunk (s % (BM / 8)) ^ 4 (k % 4), so that the
@@ -344,15 +319,15 @@ struct Dma64Cfg {
 // rows below kdim (so operands larger than 4 GiB work).
 template <class C, bool XT = false>
 struct K64Loader {
-  static_assert(!XT || (C::BUF && C::BM % 128 == 0), "k-major X: buffer loads, >= 16 chunks per k row");
+  static_assert(!XT || C::BM % 128 == 0, "k-major X: at least 16 chunks per k row");
   const bf16_t* X;
   const bf16_t* Y;
-  __amdgpu_buffer_rsrc_t rx, ry;  // (unused, and dropped by the compiler, when BUF = 0)
+  __amdgpu_buffer_rsrc_t rx, ry;
   int64_t ldx_;
   uint32_t xoff[XT ? C::X_LOADS : 1];
-  // BUF: byte offsets of this lane's first X and Y loads; load i adds i steps
-  // (the steps are workgroup-uniform).  Otherwise element offsets of every load.
-  uint32_t off[C::BUF ? 2 : C::LOADS_PER_STAGE];
+  // byte offsets of this lane's first X and Y loads; load i adds i steps (the
+  // steps are workgroup-uniform)
+  uint32_t off[2];
   uint32_t xstep, ystep;
   int wave, lchunk, kdim;
   __device__ __forceinline__ K64Loader(const bf16_t* X_, int64_t ldx, int xrows, const bf16_t* Y_, int64_t ldy,
@@ -377,21 +352,8 @@ struct K64Loader {
         xoff[i] = (uint32_t)(k * ldx * 2 + ((pc ^ (4 * (k & 3))) * 16));
       }
     }
-    if constexpr (C::BUF) {
-      off[0] = (uint32_t)((wave * 8 + lrow) * ldx * 2 + lchunk * 16);
-      off[1] = (uint32_t)((wave * 8 + lrow) * ldy * 2 + lchunk * 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::X_LOADS; ++i) {
-        const int row = (wave + i * C::NWAVES) * 8 + lrow;
-        off[i] = (uint32_t)((row < xrows ? row : 0) * ldx + lchunk * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < C::Y_LOADS; ++i) {
-        const int row = (wave + i * C::NWAVES) * 8 + lrow;
-        off[C::X_LOADS + i] = (uint32_t)((row < yrows ? row : 0) * ldy + lchunk * 8);
-      }
-    }
+    off[0] = (uint32_t)((wave * 8 + lrow) * ldx * 2 + lchunk * 16);
+    off[1] = (uint32_t)((wave * 8 + lrow) * ldy * 2 + lchunk * 16);
   }
   __device__ __forceinline__ char* lds_at(char* smem, int kt, int i) const {
     char* st = smem + (kt & 1) * C::STAGE_BYTES;
@@ -399,8 +361,7 @@ struct K64Loader {
                           : st + C::X_BYTES + (wave + (i - C::X_LOADS) * C::NWAVES) * 1024;
   }
   // load i of slice kt; `whole`: the slice lies inside [0, kdim).  Chunks past
-  // kdim load zeros: an offset past every record (buffer loads) or the zero
-  // block.
+  // kdim load zeros: an offset past every record.
   __device__ __forceinline__ void dma(char* smem, int kt, int i, bool whole) const {
     if constexpr (XT) {
       if (i < C::X_LOADS) {
@@ -411,14 +372,9 @@ struct K64Loader {
       }
     }
     const bool in = whole || kt * C::BK + lchunk * 8 < kdim;
-    if constexpr (C::BUF) {
-      // the offset is formed here rather than kept per load in registers
-      const uint32_t o = i < C::X_LOADS ? off[0] + (uint32_t)i * xstep : off[1] + (uint32_t)(i - C::X_LOADS) * ystep;
-      lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? o : kOutOfRange, (uint32_t)(kt * C::BK * 2), lds_at(smem, kt, i));
-    } else {
-      const bf16_t* src = (i < C::X_LOADS ? X : Y) + kt * C::BK + off[i];
-      lds_dma16(in ? (const void*)src : (const void*)kZeroChunk, lds_at(smem, kt, i));
-    }
+    // the offset is formed here rather than kept per load in registers
+    const uint32_t o = i < C::X_LOADS ? off[0] + (uint32_t)i * xstep : off[1] + (uint32_t)(i - C::X_LOADS) * ystep;
+    lds_dma_buf(i < C::X_LOADS ? rx : ry, in ? o : kOutOfRange, (uint32_t)(kt * C::BK * 2), lds_at(smem, kt, i));
   }
   // the first two slices (the loop's prologue)
   __device__ __forceinline__ void prologue(char* smem) const {
@@ -447,7 +403,7 @@ __device__ __forceinline__ void tile_k64_prologue(const bf16_t* __restrict__ X, 
 // past kdim reads as zero; rows past xrows / yrows give outputs that callers
 // must discard (select, never multiply).  Byte offsets BM * ldx * 2 and
 // BN * ldy * 2 must stay below 2^31.  Ends with a barrier after which the LDS
-// may be reused.  PRE (PIPE = 2 only): the prologue was issued by
+// may be reused.  PRE: the prologue was issued by
 // tile_k64_prologue with the same arguments; the loop starts by waiting for
 // every outstanding vector memory operation (stores count on this GPU).
 //
@@ -461,8 +417,7 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
                                              const bf16_t* __restrict__ Y, int64_t ldy, int yrows, int kdim,
                                              char* smem) {
   static_assert(C::BK == 64 && C::NSTAGE == 2, "two 64-wide stages");
-  static_assert(!PRE || C::PIPE == 2, "prologue issued ahead only for the substep pipeline");
-  static_assert(!XT || (C::PIPE == 2 && !PRE), "k-major X: substep pipeline, prologue issued here");
+  static_assert(!XT || !PRE, "k-major X: the prologue is issued here");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -490,70 +445,15 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
   for (int sub = 0; sub < 4; ++sub) roff[sub] = rrow * C::ROW_BYTES + (((2 * sub + (lane >> 5)) ^ rsw) * 16);
   const int xwave = wave_m * C::WM * C::ROW_BYTES;
   const int ywave = C::X_BYTES + wave_n * C::WN * C::ROW_BYTES;
-  // fragment q (substep q / (MB + NB); X blocks, then Y blocks) of the half
-  // stage `odd` of stage kt
-  auto read = [&](int kt, auto odd, Frags<C>& f, int q) {
-    const char* st = smem + (kt & 1) * C::STAGE_BYTES;
-    const int s = q / (C::MB + C::NB), w = q % (C::MB + C::NB);
-    const int sub = 2 * decltype(odd)::value + s;
-    if (w < C::MB)
-      f.a[s][w] = *reinterpret_cast<const bf16x8*>(st + xwave + w * 32 * C::ROW_BYTES + roff[sub]);
-    else
-      f.b[s][w - C::MB] = *reinterpret_cast<const bf16x8*>(st + ywave + (w - C::MB) * 32 * C::ROW_BYTES + roff[sub]);
-  };
-  constexpr int kMfma = 2 * C::MB * C::NB;
-  constexpr int kReads = 2 * (C::MB + C::NB);
   constexpr int kDma = C::LOADS_PER_STAGE;
-  auto mfma = [&](const Frags<C>& f, int j) {
-    const int s = j / (C::MB * C::NB), mb = (j / C::NB) % C::MB, nb = j % C::NB;
-    tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][mb], f.b[s][nb], tile.acc[mb][nb], 0, 0, 0);
-  };
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
-  // half-step 2 kt: the next fragments come from the same stage; the reads
-  // are spread evenly over the MFMAs
-  auto half_even = [&](int kt, const Frags<C>& cur, Frags<C>& nxt) {
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkm0();
-#pragma unroll
-    for (int j = 0; j < kMfma; ++j) {
-      mfma(cur, j);
-#pragma unroll
-      for (int q = j * kReads / kMfma; q < (j + 1) * kReads / kMfma; ++q) read(kt, Odd{}, nxt, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // half-step 2 kt + 1: refill stage kt with slice kt + 2 (its loads first,
-  // to give them the most time), then read the first half of stage kt + 1
-  auto half_odd = [&](int kt, const Frags<C>& cur, Frags<C>& nxt, bool next, bool refill, bool whole) {
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkm0();
-    if (next) {
-      wait_vmcnt<0>();
-      phase_barrier();
-    }
-#pragma unroll
-    for (int j = 0; j < kMfma; ++j) {
-      mfma(cur, j);
-#pragma unroll
-      for (int q = j * (kDma + kReads) / kMfma; q < (j + 1) * (kDma + kReads) / kMfma; ++q) {
-        if (q < kDma) {
-          if (refill) dma(kt + 2, q, whole);
-        } else if (next) {
-          read(kt + 1, Even{}, nxt, q - kDma);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
   const int nk = (kdim + C::BK - 1) / C::BK;
   const int n_full = kdim / C::BK;
-  if constexpr (C::PIPE == 2) {
-    // Substep pipeline: the fragments of k16 substep q + 1 are read under the
-    // MFMAs of substep q (two fragment sets of one substep each).  At the last
-    // substep of stage kt every wave has finished reading it: after the wait
-    // for slice kt + 1 and the barrier, stage kt is refilled with slice kt + 2.
+  {
+    // the fragments of k16 substep q + 1 are read under the MFMAs of substep
+    // q; at the last substep of stage kt every wave has finished reading it:
+    // after the wait for slice kt + 1 and the barrier, stage kt is refilled
+    // with slice kt + 2
     using SF = SubFrags<C>;
     // XT: this lane's byte offsets of its first transposing read per m block
     // (group g = lane / 16 reads k rows 8 (g / 2) + 4 h + r, columns
@@ -651,71 +551,6 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
         substep(kt, fb, fa, kt + 1, 0, next, true, kt + 2 < nk, kt + 2 < n_full);
       }
     }
-  } else if constexpr (!C::PIPE) {
-    if (nk > 0) {
-#pragma unroll
-      for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
-      if (nk > 1) {
-#pragma unroll
-        for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
-        wait_vmcnt<kDma>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      __builtin_amdgcn_s_barrier();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt > 0) {
-        // only stage kt is in flight; the barrier also ends every wave's
-        // reads of stage kt - 1, whose buffer takes slice kt + 1
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + 1 < nk) {
-          const bool whole = kt + 1 < n_full;
-#pragma unroll
-          for (int i = 0; i < kDma; ++i) dma(kt + 1, i, whole);
-        }
-      }
-      const char* st = smem + (kt & 1) * C::STAGE_BYTES;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        bf16x8 a[C::MB], b[C::NB];
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-          a[mb] = *reinterpret_cast<const bf16x8*>(st + xwave + mb * 32 * C::ROW_BYTES + roff[sub]);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-          b[nb] = *reinterpret_cast<const bf16x8*>(st + ywave + nb * 32 * C::ROW_BYTES + roff[sub]);
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            tile.acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], tile.acc[mb][nb], 0, 0, 0);
-      }
-    }
-  } else if (nk > 0) {
-#pragma unroll
-    for (int i = 0; i < kDma; ++i) dma(0, i, n_full > 0);
-    if (nk > 1) {
-#pragma unroll
-      for (int i = 0; i < kDma; ++i) dma(1, i, n_full > 1);
-      wait_vmcnt<kDma>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    phase_barrier();
-    Frags<C> fa, fb;
-#pragma unroll
-    for (int q = 0; q < kReads; ++q) read(0, Even{}, fa, q);
-    int kt = 0;
-    for (; kt + 2 < n_full; ++kt) {  // steady state: the refilled slice is whole
-      half_even(kt, fa, fb);
-      half_odd(kt, fb, fa, true, true, true);
-    }
-    for (; kt < nk; ++kt) {
-      half_even(kt, fa, fb);
-      half_odd(kt, fb, fa, kt + 1 < nk, kt + 2 < nk, kt + 2 < n_full);
-    }
   }
   __syncthreads();
 }
@@ -749,8 +584,8 @@ __device__ __forceinline__ void grouped_mn(int L, int tiles_m, int tiles_n, int 
 // Configurations whose loop can take a prologue issued ahead (tile_k64_prologue).
 template <class C>
 struct PrefetchOK : std::false_type {};
-template <int BM, int BN, int WM, int WN, int BUF>
-struct PrefetchOK<Dma64Cfg<BM, BN, WM, WN, 2, BUF>> : std::true_type {};
+template <int BM, int BN, int WM, int WN>
+struct PrefetchOK<Dma64Cfg<BM, BN, WM, WN>> : std::true_type {};
 
 // One entry point for both main loops.
 template <class C>
