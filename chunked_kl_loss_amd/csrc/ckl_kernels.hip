@@ -650,7 +650,9 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   using TIn = typename C::TIn;
   // bf16 256 x 256 tiles leave the kernel through the LDS (the whole tile,
   // 128 KiB, once the main loop is done with it) as 16-byte stores that
-  // form 512-byte runs of G and G^T rows; otherwise straight from registers.
+  // form 512-byte runs of G rows (and of G^T rows when Gt is not null);
+  // otherwise straight from registers.  Staging also frees the registers the
+  // substep pipeline of the main loop needs.
   constexpr bool kStage = std::is_same<TIn, bf16_t>::value && C::BM == 256 && C::BN == 256 && C::WM == 128 &&
                           C::LDS_BYTES >= 256 * 256 * 2;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
