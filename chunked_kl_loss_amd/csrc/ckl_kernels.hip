@@ -771,7 +771,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
       __syncthreads();
       const int tid = threadIdx.x;
       bf16_t* Gtile = G + (int64_t)(t0 - tb0) * ldG + (v0 - vb0);
-      bf16_t* Gttile = Gt + (int64_t)(v0 - vb0) * ldGt + (t0 - tb0);
+      // (offset of the G^T tile; a pointer is formed only when there is a G^T)
+      const int64_t gt_origin = (int64_t)(v0 - vb0) * ldGt + (t0 - tb0);
       // G rows: 32 threads per token row of 256 entries (512 bytes)
 #pragma unroll 2
       for (int pass = 0; pass < 256 / (C::NTHREADS / 32); ++pass) {
@@ -796,8 +797,9 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
             lo[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x05040100u);
             hi[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x07060302u);
           }
-          *reinterpret_cast<u32x4*>(Gttile + (int64_t)(vb * 8 + 2 * w) * ldGt + tq * 8) = lo;
-          *reinterpret_cast<u32x4*>(Gttile + (int64_t)(vb * 8 + 2 * w + 1) * ldGt + tq * 8) = hi;
+          bf16_t* gt = Gt + gt_origin + (int64_t)(vb * 8 + 2 * w) * ldGt + tq * 8;
+          *reinterpret_cast<u32x4*>(gt) = lo;
+          *reinterpret_cast<u32x4*>(gt + ldGt) = hi;
         }
       }
       __syncthreads();  // the next tile's loads refill the LDS
