@@ -189,8 +189,8 @@ def test_fused_logprob_teacher():
 
 
 def test_fused_odd_chunk_count():
-    # three 256-row chunks (the last ragged): the dW update of the last group
-    # covers one chunk only
+    # three 256-row chunks (the last ragged) in one dW group: the update's k
+    # range ends inside the last chunk
     import chunked_kl_loss_amd as ckl
     x = inputs(1, T=700)
     plan = ckl.fused_plan(ckl.make_problem(x.T, x.d, x.V, x.K, 200))
@@ -198,6 +198,19 @@ def test_fused_odd_chunk_count():
     say(f"case fused odd chunk count T={x.T} plan={plan}")
     got = run_gpu_fused(x, chunk=200, grad_loss=1.25)
     check_full(x, got, oracle_full(x, grad_loss=1.25), TOL["bf16"], 2e-3)
+
+
+def test_fused_partial_last_dw_group():
+    # eleven 256-row chunks: a full group of eight, then a group of three
+    # whose last chunk holds 40 rows (the dW update reads G k-major over
+    # 2 * 256 + 256 rows of the second group)
+    import chunked_kl_loss_amd as ckl
+    x = inputs(1, T=2600)
+    plan = ckl.fused_plan(ckl.make_problem(x.T, x.d, x.V, x.K, 256))
+    assert plan["chunks"] == 11 and plan["rows"] == 256
+    say(f"case fused partial last dW group T={x.T} plan={plan}")
+    got = run_gpu_fused(x, chunk=256, grad_loss=0.75)
+    check_full(x, got, oracle_full(x, grad_loss=0.75), TOL["bf16"], 2e-3)
 
 
 def test_fused_clustered_teacher_indices():
