@@ -432,8 +432,6 @@ __device__ __forceinline__ void tile_mma_k64(DmaTile<C>& tile, const bf16_t* __r
       for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = 0.f;
 
   const K64Loader<C, XT> ld(X, ldx, xrows, Y, ldy, yrows, kdim);
-  const int lchunk = ld.lchunk;
-  (void)lchunk;
   auto dma = [&](int kt, int i, bool whole) { ld.dma(smem, kt, i, whole); };
 
   // Reader: lane reads row (lane & 31) + 32 block of its wave's rows, chunk
