@@ -1486,7 +1486,9 @@ static hipError_t gemm_pair_t(const GemmArgs& a0, const GemmArgs& a1, hipStream_
     p[i].yb = a[i]->yb;
     p[i].ob = a[i]->ob;
     p[i].xt = a[i]->xt;
-    if (a[i]->xt && (!kXtOK<C> || a[i]->batches > 1)) return hipErrorInvalidValue;
+    // k-major X: every tile reads BM whole columns of each k row
+    if (a[i]->xt && (!kXtOK<C> || a[i]->batches > 1 || (int64_t)(a[i]->M + C::BM - 1) / C::BM * C::BM > a[i]->ldx))
+      return hipErrorInvalidValue;
     p[i].tiles_m = a[i]->M > 0 ? (a[i]->M + C::BM - 1) / C::BM : 0;
     p[i].tiles = a[i]->M > 0 && a[i]->N > 0 ? p[i].tiles_m * ((a[i]->N + C::BN - 1) / C::BN) * p[i].batches : 0;
   }
