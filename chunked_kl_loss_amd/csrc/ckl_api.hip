@@ -50,10 +50,11 @@ constexpr int64_t kCUs = 256;
 // main loop (a 256 x 256 fp32 tile at one CU's share of HBM bandwidth).
 constexpr int64_t kMaxSplit = 64;
 constexpr int64_t kEpilogueK = 512;
-// Fused call: G^T keeps the columns of up to this many consecutive row
-// chunks, so the dW update (an fp32 read-modify-write of all of dW) runs once
-// per group with k = group * chunk rows instead of once per chunk.
-constexpr int64_t kDwChunks = 8;
+// Fused call: G (bf16; G^T for fp32) of consecutive row chunks is kept for
+// up to this many rows, so the dW update (an fp32 read-modify-write of all
+// of dW) runs once per group of chunks with k = group rows instead of once
+// per chunk; the buffer's size does not grow with the chunk size.
+constexpr int64_t kDwRows = 16384;
 // Row padding (elements) of G^T in the fused call (fp32; bf16 keeps no G^T).
 // Its rows are written in short runs for consecutive rows; some strides put
 // those runs on few memory channels (with eight 2048-row chunks of bf16, a
@@ -230,7 +231,7 @@ Plan make_plan(const ckl_problem* p) {
   // block sums are per 256 rows), at most the padded row count.
   q.Cs = std::min(round_up(p->chunk, 256), round_up(q.Tp, 256));
   q.nS = ceil_div(q.Tp, q.Cs);
-  q.Gc = std::min(kDwChunks, q.nS);  // chunks per dW group
+  q.Gc = std::max<int64_t>(1, std::min(kDwRows / q.Cs, q.nS));  // chunks per dW group
   pick_splits(q.Cs / q.BN, q.Vp / q.BM, &q.c_splits, &q.c_tps);
   // dH split-k parts: the count whose tiles finish in the fewest k-steps when
   // dealt to kCUs workgroups in rounds (whole rounds: a launch that holds only

@@ -175,11 +175,11 @@ ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
  * rounding of the non-teacher entries of G to in_dtype (u is rounded before
  * it is rescaled).
  *   ws: device workspace of at least ckl_workspace_size(p, 2) bytes: with
- *   n = min(8, number of chunks), n + 1 chunk x V buffers of in_dtype (bf16:
- *   the forward's exponentials u of one chunk and G of n consecutive chunks;
- *   fp32: G of one chunk and G^T of n chunks; the fp32 update of dW runs
- *   once per n chunks), H^T and W^T, the dH split-k partials and small
- *   per-row arrays.
+ *   n = the number of chunks, at most 16384 rows' worth and at least one,
+ *   n + 1 chunk x V buffers of in_dtype (bf16: the forward's exponentials u
+ *   of one chunk and G of n consecutive chunks; fp32: G of one chunk and G^T
+ *   of n chunks; the fp32 update of dW runs once per n chunks), H^T and W^T,
+ *   the dH split-k partials and small per-row arrays.
  * Rows per chunk: `chunk` rounded up to whole tiles (256 rows for bf16,
  * 128 for fp32), at most T rounded up. */
 ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void* W,
