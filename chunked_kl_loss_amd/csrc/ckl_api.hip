@@ -267,7 +267,8 @@ FwdWs fwd_layout(const Plan& q) {
   w.zg_s = take(q.T * q.K * 4);
   w.E = take(q.T * 4);
   w.M = take(q.T * 4);
-  w.part = take(q.f_splits * q.T * 8);
+  // split LSE states: of all rows (shard forward) or of one chunk (forward)
+  w.part = take(std::max(q.f_splits * q.T, q.c_splits * q.Cs) * 8);
   w.blk = take(q.T * 8);  // per-row fp64 loss terms
   w.N = take(4);
   w.bad = take(4);
@@ -420,18 +421,32 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
-                [&] {
-                  return ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits,
-                                             (int)q.f_tps, nullptr, 0, nullptr, 0, st);
-                }),
-          "fwd_lse");
-  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
-                [&] {
-                  return ckl::launch_fwd_finalize(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, E, M, mask, lse,
-                                                  row_loss, (double*)(b + w.blk), N, loss, st);
-                }),
-          "fwd_finalize");
+  // chunk by chunk ([README] Full Chunked KL): a chunk's logit tiles give its
+  // rows' split LSE states and teacher logits, then its rows' LSE and loss
+  // terms; the vocabulary sweep of one chunk shares each W tile between the
+  // chunk's row blocks while it is in the L2
+  double* blk = (double*)(b + w.blk);
+  for (int64_t c = 0; c < q.nS; ++c) {
+    const int64_t tb0 = c * q.Cs;
+    const int rows = (int)std::min(q.Cs, q.T - tb0);
+    if (rows <= 0) break;
+    const char* Hc = (const char*)H + tb0 * q.d * q.esz;
+    HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
+                  [&] {
+                    return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0, st);
+                  }),
+            "fwd_lse");
+    HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                  [&] {
+                    return ckl::launch_fwd_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K, zg_s + tb0 * K,
+                                                E + tb0, M + tb0, mask ? mask + tb0 : nullptr, lse + tb0,
+                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0, st);
+                  }),
+            "fwd_rows");
+  }
+  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st, [&] { return ckl::launch_loss_reduce(blk, T, N, loss, st); }),
+          "loss_reduce");
   return CKL_OK;
 }
 

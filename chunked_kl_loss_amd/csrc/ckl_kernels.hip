@@ -1387,14 +1387,6 @@ hipError_t launch_loss_reduce(const double* row_ld, int T, const int* N, float* 
   return hipSuccess;
 }
 
-hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
-                               const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
-                               float* row_loss, double* row_ld, const int* N, float* loss, hipStream_t st) {
-  hipError_t e = launch_fwd_rows(part, S, T, K, p_s, zg_s, Erow, Mrow, mask, lse, row_loss, row_ld, st);
-  if (e != hipSuccess) return e;
-  return launch_loss_reduce(row_ld, T, N, loss, st);
-}
-
 hipError_t launch_fwd_shard_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                                  float* lse_part, float* cross_part, hipStream_t st) {
   hipLaunchKernelGGL(fwd_shard_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, st, (const float2*)part, S, T, K, p_s,

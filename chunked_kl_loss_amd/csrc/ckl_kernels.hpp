@@ -30,16 +30,14 @@ hipError_t launch_shard_combine(const float* lse_parts, const float* cross_parts
 hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
                           float* zg_s, void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG,
                           float* mtab, int64_t ldm, hipStream_t st);
-// Per-row LSE and loss plus per-256-row fp64 sums; then the mean over N.
+// Per-row LSE and loss of rows [0, T) of `part` (S split states per row),
+// and each row's loss term in fp64 at row_ld[t] (0 for masked rows).
 hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                            const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
                            double* row_ld, hipStream_t st);
 // loss = sum of row_ld[0 .. T) (fp64, fixed order) / *N
 hipError_t launch_loss_reduce(const double* row_ld, int T, const int* N, float* loss, hipStream_t st);
-hipError_t launch_fwd_finalize(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
-                               const float* Erow, const float* Mrow, const uint8_t* mask, float* lse,
-                               float* row_loss, double* row_ld, const int* N, float* loss, hipStream_t st);
-// Fused path, after the rows' LSE is known: G[t][v] (holding u) becomes
+// Fused path, fp32, after the rows' LSE is known: G[t][v] (holding u) becomes
 // g = s_t M_t u 2^(m - lse_t log2e) in place, zero for t >= rows, v >= V or
 // s_t = 0, and G^T[v][t] = g, over t < rows_p and v < Vp (tile multiples).
 hipError_t launch_gpass(int in_bf16, void* G, int64_t ldG, void* Gt, int64_t ldGt, const float* mtab, int64_t ldm,
