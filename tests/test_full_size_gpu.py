@@ -126,11 +126,12 @@ def test_packed_documents_chunk_sweep():
         if base is None:
             base = got
         else:
-            # the forward does not depend on chunk; the backward only reorders
-            # fp32 sums between G blocks (dW is fp32 out; dH is bf16 out, where
-            # a reordered sum may round one bf16 ulp = 2^-8 apart)
-            assert got["loss"] == base["loss"]
-            assert np.array_equal(got["lse"], base["lse"])
+            # chunk only reorders fp32 sums: the forward's merge of each row's
+            # vocabulary-split states (the splits follow the chunk's tiles) and
+            # the backward's sums between G blocks (dW is fp32 out; dH is bf16
+            # out, where a reordered sum may round one bf16 ulp = 2^-8 apart)
+            assert got["loss"] == pytest.approx(base["loss"], rel=1e-6)
+            assert np.abs(got["lse"] - base["lse"]).max() <= 1e-5 * np.abs(base["lse"]).max()
             scale = np.abs(base["dW"]).max()
             assert np.abs(got["dW"] - base["dW"]).max() <= 1e-3 * scale
             assert np.abs(got["dH"] - base["dH"]).max() <= TOL["bf16"]["grad_rel"] * np.abs(base["dH"]).max()
