@@ -132,12 +132,11 @@ struct Plan {
   int64_t esz;
   int64_t BM, BN;  // logit tile: vocabulary rows x token rows
   int64_t Tp, Vp;
-  // forward
-  int64_t f_splits, f_tps;
   // backward G blocks
   int64_t Tc, Vc, nT, nV;
-  // fused forward + backward: row chunks of Cs rows, nS of them; forward
-  // splits per chunk; dH split-k into Sh parts of Vs vocabulary columns
+  // row chunks of Cs rows, nS of them (both forwards; the fused backward),
+  // vocabulary splits per chunk; dH split-k into Sh parts of Vs vocabulary
+  // columns (fused)
   int64_t Cs, nS, Gc, c_splits, c_tps, Sh, Vs, groups;
 };
 
@@ -202,7 +201,6 @@ Plan make_plan(const ckl_problem* p) {
   q.BN = ckl::tile_rows_n(q.in_bf16);
   q.Tp = round_up(q.T, q.BN);
   q.Vp = round_up(q.V, q.BM);
-  pick_splits(ceil_div(q.T, q.BN), ceil_div(q.V, q.BM), &q.f_splits, &q.f_tps);
 
   // G blocks of Tc token rows x Vc vocabulary columns, both stored twice (G and
   // G^T), within chunk * V elements in total.  Among the admissible shapes pick
@@ -267,8 +265,7 @@ FwdWs fwd_layout(const Plan& q) {
   w.zg_s = take(q.T * q.K * 4);
   w.E = take(q.T * 4);
   w.M = take(q.T * 4);
-  // split LSE states: of all rows (shard forward) or of one chunk (forward)
-  w.part = take(std::max(q.f_splits * q.T, q.c_splits * q.Cs) * 8);
+  w.part = take(q.c_splits * q.Cs * 8);  // split LSE states of one chunk
   w.blk = take(q.T * 8);  // per-row fp64 loss terms
   w.N = take(4);
   w.bad = take(4);
@@ -716,18 +713,25 @@ ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
-                [&] {
-                  return ckl::launch_fwd_lse(q.in_bf16, H, W, T, d, V, K, idx_s, zg_s, b + w.part, (int)q.f_splits,
-                                             (int)q.f_tps, nullptr, 0, nullptr, 0, st);
-                }),
-          "fwd_lse");
-  HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
-                [&] {
-                  return ckl::launch_fwd_shard_rows(b + w.part, (int)q.f_splits, T, K, p_s, zg_s, lse_part,
-                                                    cross_part, st);
-                }),
-          "fwd_shard_rows");
+  // chunk by chunk, as ckl_forward
+  for (int64_t c = 0; c < q.nS; ++c) {
+    const int64_t tb0 = c * q.Cs;
+    const int rows = (int)std::min(q.Cs, q.T - tb0);
+    if (rows <= 0) break;
+    const char* Hc = (const char*)H + tb0 * q.d * q.esz;
+    HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
+                  [&] {
+                    return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0, st);
+                  }),
+            "fwd_lse");
+    HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
+                  [&] {
+                    return ckl::launch_fwd_shard_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K,
+                                                      zg_s + tb0 * K, lse_part + tb0, cross_part + tb0, st);
+                  }),
+            "fwd_shard_rows");
+  }
   return CKL_OK;
 }
 

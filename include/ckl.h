@@ -87,9 +87,10 @@ typedef struct {
   int64_t d;      /* hidden size, >= 8 and a multiple of 8                 */
   int64_t V;      /* vocabulary size, 1 .. 4,000,000                       */
   int64_t K;      /* teacher entries per row, 1 <= K <= min(V, 4096)       */
-  int64_t chunk;  /* backward G-block budget in rows of V entries, >= 1:   */
-                  /* the backward keeps at most about chunk*V logit        */
-                  /* gradients at a time (rounded up to whole tiles).      */
+  int64_t chunk;  /* rows per chunk, >= 1: the forwards project chunk     */
+                  /* rows at a time (rounded up to whole tiles); the       */
+                  /* backward keeps at most about chunk*V logit gradients  */
+                  /* at a time.                                            */
   int32_t in_dtype;  /* ckl_dtype of H and W                               */
   int32_t dh_dtype;  /* ckl_dtype of dH                                    */
   int32_t dw_dtype;  /* ckl_dtype of dW                                    */
@@ -121,8 +122,10 @@ ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes);
  *   row_loss: [T] device float32 or NULL; l_t for kept rows, 0 for masked.
  *   ws:       device workspace of at least ckl_workspace_size(p, 0) bytes;
  *             its contents on entry do not matter.
- * The loss and its logit-gradient formula follow the objective section and
- * the Full Chunked KL paragraph of the README page named above. */
+ * Rows are projected one chunk at a time; the logits never leave the MFMA
+ * accumulators.  The loss and its logit-gradient formula follow the
+ * objective section and the Full Chunked KL paragraph of the README page
+ * named above. */
 ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W,
                        const int32_t* idx, const float* tlogit, const uint8_t* mask,
                        float* loss, float* lse, float* row_loss,
