@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     forward,
     forward_backward,
     fused_plan,
+    scale_cast,
     load_library,
     make_problem,
     shard_combine,

@@ -30,6 +30,7 @@ EXPORTED = (
     "ckl_backward_plan",
     "ckl_forward_backward",
     "ckl_fused_plan",
+    "ckl_scale_cast",
     "ckl_shard_forward",
     "ckl_shard_combine",
     "ckl_timing_enable",
@@ -60,6 +61,9 @@ class Problem(ctypes.Structure):
         ("teacher_form", ctypes.c_int32),
         ("v_offset", ctypes.c_int64),
         ("v_total", ctypes.c_int64),
+        ("dw_group_rows", ctypes.c_int64),
+        ("compact_mask", ctypes.c_int32),
+        ("reserved_", ctypes.c_int32),
     ]
 
 
@@ -90,6 +94,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckl_forward_backward.restype = i32
     lib.ckl_fused_plan.argtypes = [P, i64p]
     lib.ckl_fused_plan.restype = i32
+    lib.ckl_scale_cast.argtypes = [vp, vp, ctypes.c_int64, i32, vp, vp]
+    lib.ckl_scale_cast.restype = i32
     lib.ckl_shard_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ckl_shard_forward.restype = i32
     lib.ckl_shard_combine.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -116,10 +122,11 @@ def check(status: int, lib=None) -> None:
 
 
 def make_problem(T, d, V, K, chunk, in_dtype=CKL_BF16, dh_dtype=None, dw_dtype=CKL_F32, validate=False,
-                 teacher_form=CKL_TEACHER_LOGITS, v_offset=0, v_total=0) -> Problem:
+                 teacher_form=CKL_TEACHER_LOGITS, v_offset=0, v_total=0, dw_group_rows=0,
+                 compact_mask=False) -> Problem:
     return Problem(int(T), int(d), int(V), int(K), int(chunk), int(in_dtype),
                    int(in_dtype if dh_dtype is None else dh_dtype), int(dw_dtype), int(bool(validate)),
-                   int(teacher_form), int(v_offset), int(v_total))
+                   int(teacher_form), int(v_offset), int(v_total), int(dw_group_rows), int(bool(compact_mask)), 0)
 
 
 def workspace_size(prob: Problem, which: int) -> int:
@@ -137,11 +144,11 @@ def backward_plan(prob: Problem):
 
 
 def fused_plan(prob: Problem):
-    """Row chunks and dH split-k of ckl_forward_backward for this problem."""
+    """Row chunks, dH split-k and dW groups of ckl_forward_backward for this problem."""
     lib = load_library()
-    out = (ctypes.c_int64 * 4)()
+    out = (ctypes.c_int64 * 5)()
     check(lib.ckl_fused_plan(ctypes.byref(prob), out), lib)
-    return dict(rows=out[0], chunks=out[1], dh_parts=out[2], part_cols=out[3])
+    return dict(rows=out[0], chunks=out[1], dh_parts=out[2], part_cols=out[3], dw_group_chunks=out[4])
 
 
 KERNEL_CLASSES = ("teacher_prep", "fwd_lse", "fwd_finalize", "bwd_grad", "gemm_dhdw", "g_pass", "transpose",
@@ -213,14 +220,16 @@ def _stream_ptr(device):
 
 
 def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = False,
-            want_row_loss: bool = False, teacher_form: int = CKL_TEACHER_LOGITS):
+            want_row_loss: bool = False, teacher_form: int = CKL_TEACHER_LOGITS, compact_mask: bool = True):
     """Returns (loss [1] float32, lse [T] float32, row_loss [T] or None).  tlogit holds teacher logits
-    (teacher_form 0) or truncated teacher log-probabilities used as given (teacher_form 1)."""
+    (teacher_form 0) or truncated teacher log-probabilities used as given (teacher_form 1).
+    compact_mask: with a mask, only the kept rows are computed (packed first)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
     T, d = H.shape
     V, K = W.shape[0], idx.shape[1]
-    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate, teacher_form=teacher_form)
+    prob = make_problem(T, d, V, K, chunk, _dtype_code(H.dtype), validate=validate, teacher_form=teacher_form,
+                        compact_mask=compact_mask and mask is not None)
     lib = load_library()
     ws_bytes = workspace_size(prob, 0)
     dev = H.device
@@ -236,7 +245,7 @@ def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = Fa
 
 def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh_dtype=None,
              dw_dtype=None, validate: bool = False, teacher_form: int = CKL_TEACHER_LOGITS,
-             v_offset: int = 0, v_total: int = 0):
+             v_offset: int = 0, v_total: int = 0, compact_mask: bool = True):
     """Returns (dH, dW) of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
@@ -245,7 +254,8 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     in_code = _dtype_code(H.dtype)
     dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
     dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
-    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form, v_offset, v_total)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form, v_offset, v_total,
+                        compact_mask=compact_mask and mask is not None)
     lib = load_library()
     ws_bytes = workspace_size(prob, 1)
     dev = H.device
@@ -262,9 +272,10 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
 
 def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 2048, dh_dtype=None,
                      dw_dtype=None, validate: bool = False, want_row_loss: bool = False,
-                     teacher_form: int = CKL_TEACHER_LOGITS):
+                     teacher_form: int = CKL_TEACHER_LOGITS, compact_mask: bool = True, dw_group_rows: int = 0):
     """One call, no logit recompute: returns (loss [1], lse [T], row_loss [T] or None, dH, dW), the
-    gradients being those of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
+    gradients being those of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1).
+    dw_group_rows: rows of logit gradients kept per dW update (0 = the library default)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
     T, d = H.shape
@@ -272,7 +283,8 @@ def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 
     in_code = _dtype_code(H.dtype)
     dh_code = in_code if dh_dtype is None else _dtype_code(dh_dtype)
     dw_code = CKL_F32 if dw_dtype is None else _dtype_code(dw_dtype)
-    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form)
+    prob = make_problem(T, d, V, K, chunk, in_code, dh_code, dw_code, validate, teacher_form,
+                        dw_group_rows=dw_group_rows, compact_mask=compact_mask and mask is not None)
     lib = load_library()
     ws_bytes = workspace_size(prob, 2)
     dev = H.device
@@ -334,3 +346,19 @@ def shard_combine(lse_parts, cross_parts, idx, tlogit, mask=None, v_total: int =
                                 _ptr(tlogit), _ptr(m), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws_bytes,
                                 _stream_ptr(dev)), lib)
     return loss, lse, row_loss
+
+
+def scale_cast(src, dst, scale=None):
+    """dst = scale * src rounded once to dst's dtype (src float32; dst float32 or bfloat16, same number
+    of elements; scale: [1] float32 tensor or None = 1).  Returns dst."""
+    torch = _torch()
+    if not (src.is_cuda and dst.is_cuda) or src.dtype != torch.float32 or src.numel() != dst.numel():
+        raise ValueError("src must be a float32 GPU tensor with as many elements as dst")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    lib = load_library()
+    if scale is not None:
+        scale = scale.to(device=src.device, dtype=torch.float32).contiguous()
+    check(lib.ckl_scale_cast(_ptr(src), _ptr(dst), int(src.numel()), _dtype_code(dst.dtype), _ptr(scale),
+                             _stream_ptr(src.device)), lib)
+    return dst

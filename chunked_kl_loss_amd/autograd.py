@@ -4,8 +4,10 @@ ChunkedKLLoss: the forward saves (H, W, idx, tlogit, mask, lse) and the
 backward recomputes the logit tiles inside libckl.
 
 FusedChunkedKLLoss: one library call in the forward computes the loss and the
-gradients of the loss itself (no recompute); the backward only scales them by
-the incoming gradient (1 for a loss that is backpropagated directly)."""
+fp32 gradients of the loss itself (no recompute); the backward multiplies them
+by the incoming gradient and rounds them once to the dtypes of H and W, in the
+library (ckl_scale_cast).  When neither H nor W needs a gradient the forward
+computes the loss alone."""
 from __future__ import annotations
 
 import torch
@@ -25,28 +27,46 @@ class ChunkedKLLoss(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad):
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (need_h or need_w):
+            return None, None, None, None, None, None, None
         H, W, idx, tlogit, lse, mask = ctx.saved_tensors
         mask = mask if ctx.has_mask else None
         g = grad.reshape(1).to(torch.float32)
         dH, dW = _binding.backward(H, W, idx, tlogit, mask, lse, g, chunk=ctx.chunk,
                                    dh_dtype=H.dtype, dw_dtype=W.dtype, teacher_form=ctx.teacher_form)
-        return dH, dW, None, None, None, None, None
+        return (dH if need_h else None), (dW if need_w else None), None, None, None, None, None
 
 
 class FusedChunkedKLLoss(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048, teacher_form: int = 0):
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        ctx.dtypes = (H.dtype, W.dtype)
+        if not (need_h or need_w):
+            loss, _, _ = _binding.forward(H, W, idx, tlogit, mask, chunk=chunk, teacher_form=teacher_form)
+            ctx.save_for_backward(torch.empty(0, device=H.device), torch.empty(0, device=H.device))
+            return loss[0]
+        # gradients of the loss itself, kept in fp32 until the incoming
+        # gradient is known
         loss, _, _, dH, dW = _binding.forward_backward(H, W, idx, tlogit, mask, None, chunk=chunk,
-                                                       dh_dtype=H.dtype, dw_dtype=W.dtype,
+                                                       dh_dtype=torch.float32, dw_dtype=torch.float32,
                                                        teacher_form=teacher_form)
-        ctx.save_for_backward(dH, dW)
+        ctx.save_for_backward(dH if need_h else torch.empty(0, device=H.device),
+                              dW if need_w else torch.empty(0, device=H.device))
         return loss[0]
 
     @staticmethod
     def backward(ctx, grad):
-        dH, dW = ctx.saved_tensors
-        g = grad.to(torch.float32)
-        return ((dH.float() * g).to(dH.dtype), (dW.float() * g).to(dW.dtype), None, None, None, None, None)
+        dH32, dW32 = ctx.saved_tensors
+        h_dtype, w_dtype = ctx.dtypes
+        g = grad.reshape(1).to(torch.float32)
+        dH = dW = None
+        if ctx.needs_input_grad[0]:
+            dH = _binding.scale_cast(dH32, torch.empty(dH32.shape, dtype=h_dtype, device=dH32.device), g)
+        if ctx.needs_input_grad[1]:
+            dW = _binding.scale_cast(dW32, torch.empty(dW32.shape, dtype=w_dtype, device=dW32.device), g)
+        return dH, dW, None, None, None, None, None
 
 
 def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False, teacher_form: int = 0):

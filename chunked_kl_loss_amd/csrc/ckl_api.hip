@@ -51,10 +51,12 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kMaxSplit = 64;
 constexpr int64_t kEpilogueK = 512;
 // Fused call: G (bf16; G^T for fp32) of consecutive row chunks is kept for
-// up to this many rows, so the dW update (an fp32 read-modify-write of all
-// of dW) runs once per group of chunks with k = group rows instead of once
-// per chunk; the buffer's size does not grow with the chunk size.
+// a group of chunks, so the dW update (an fp32 read-modify-write of all of
+// dW) runs once per group with k = group rows instead of once per chunk.
+// Default group: at most kDwRows rows and at most kDwChunks chunks, so that a
+// smaller chunk also holds less (ckl_problem.dw_group_rows overrides it).
 constexpr int64_t kDwRows = 16384;
+constexpr int64_t kDwChunks = 8;
 // Row padding (elements) of G^T in the fused call (fp32; bf16 keeps no G^T).
 // Its rows are written in short runs for consecutive rows; some strides put
 // those runs on few memory channels (with eight 2048-row chunks of bf16, a
@@ -189,6 +191,9 @@ ckl_status check_problem(const ckl_problem* p) {
   if (p->validate != 0 && p->validate != 1) return fail(CKL_ERR_INVALID_ARG, "validate must be 0 or 1");
   if (p->teacher_form != CKL_TEACHER_LOGITS && p->teacher_form != CKL_TEACHER_LOGPROBS)
     return fail(CKL_ERR_INVALID_ARG, "teacher_form must be CKL_TEACHER_LOGITS (0) or CKL_TEACHER_LOGPROBS (1)");
+  if (p->dw_group_rows < 0) return fail(CKL_ERR_INVALID_ARG, "dw_group_rows must be >= 0");
+  if (p->compact_mask != 0 && p->compact_mask != 1) return fail(CKL_ERR_INVALID_ARG, "compact_mask must be 0 or 1");
+  if (p->reserved_ != 0) return fail(CKL_ERR_INVALID_ARG, "reserved_ must be 0");
   return CKL_OK;
 }
 
@@ -229,7 +234,10 @@ Plan make_plan(const ckl_problem* p) {
   // block sums are per 256 rows), at most the padded row count.
   q.Cs = std::min(round_up(p->chunk, 256), round_up(q.Tp, 256));
   q.nS = ceil_div(q.Tp, q.Cs);
-  q.Gc = std::max<int64_t>(1, std::min(kDwRows / q.Cs, q.nS));  // chunks per dW group
+  {
+    const int64_t group_rows = p->dw_group_rows > 0 ? p->dw_group_rows : std::min(kDwRows, kDwChunks * q.Cs);
+    q.Gc = std::max<int64_t>(1, std::min(group_rows / q.Cs, q.nS));  // chunks per dW group
+  }
   pick_splits(q.Cs / q.BN, q.Vp / q.BM, &q.c_splits, &q.c_tps);
   // dH split-k parts: the count whose tiles finish in the fewest k-steps when
   // dealt to kCUs workgroups in rounds (whole rounds: a launch that holds only
@@ -253,10 +261,30 @@ Plan make_plan(const ckl_problem* p) {
   return q;
 }
 
+// Packed rows (compact_mask with a mask): the kept rows' positions, each
+// row's rank, their number, a packed copy of their H rows and packed per-row
+// results, laid out after a call's own workspace.
+struct PackWs {
+  size_t perm, rank, N, Hc, lse, rl, total;
+};
+PackWs pack_layout(const Plan& q, size_t o) {
+  PackWs w{};
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+  w.perm = take(q.T * 4);
+  w.rank = take(q.T * 4);
+  w.N = take(4);
+  w.Hc = take((size_t)q.T * q.d * q.esz);
+  w.lse = take(q.T * 4);
+  w.rl = take(q.T * 4);
+  w.total = o;
+  return w;
+}
+
 struct FwdWs {
   size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, total;
+  PackWs pk;
 };
-FwdWs fwd_layout(const Plan& q) {
+FwdWs fwd_layout(const Plan& q, const ckl_problem* p) {
   FwdWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
@@ -270,11 +298,16 @@ FwdWs fwd_layout(const Plan& q) {
   w.N = take(4);
   w.bad = take(4);
   w.total = o;
+  if (p->compact_mask) {
+    w.pk = pack_layout(q, o);
+    w.total = w.pk.total;
+  }
   return w;
 }
 
 struct BwdWs {
   size_t idx_s, p_s, M, s, N, bad, Ht, Wt, G[kGBuffers], Gt[kGBuffers], dH, dW, total;
+  PackWs pk;
 };
 BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   BwdWs w{};
@@ -293,14 +326,21 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
     w.G[i] = take((size_t)q.Tc * (q.Vc + kLdPad) * q.esz);
     w.Gt[i] = q.in_bf16 ? 0 : take((size_t)q.Vc * (q.Tc + kLdPad) * q.esz);
   }
-  w.dH = p->dh_dtype == CKL_BF16 ? take((size_t)q.T * q.d * 4) : 0;
+  // fp32 accumulator of dH when dH is bf16, or when packed rows are
+  // scattered back at the end
+  w.dH = (p->dh_dtype == CKL_BF16 || p->compact_mask) ? take((size_t)q.T * q.d * 4) : 0;
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
   w.total = o;
+  if (p->compact_mask) {
+    w.pk = pack_layout(q, o);
+    w.total = w.pk.total;
+  }
   return w;
 }
 
 struct FusedWs {
   size_t idx_s, p_s, zg_s, E, M, part, blk, N, bad, s, Ht, Wt, U, G, Gt, mtab, dHp, dW, total;
+  PackWs pk;
 };
 FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   FusedWs w{};
@@ -329,6 +369,10 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   w.dHp = take((size_t)q.Sh * q.Cs * q.d * 4);
   w.dW = p->dw_dtype == CKL_BF16 ? take((size_t)q.V * q.d * 4) : 0;
   w.total = o;
+  if (p->compact_mask) {
+    w.pk = pack_layout(q, o);
+    w.total = w.pk.total;
+  }
   return w;
 }
 
@@ -348,6 +392,38 @@ CombineWs combine_layout(const Plan& q) {
   w.bad = take(4);
   w.total = o;
   return w;
+}
+
+// Device pointers of the packed-row area of a workspace (all NULL when the
+// call does not pack).
+struct Packed {
+  int* perm = nullptr;
+  int* rank = nullptr;
+  int* N = nullptr;
+  void* Hc = nullptr;
+  float* lse = nullptr;
+  float* rl = nullptr;
+  bool on() const { return perm != nullptr; }
+};
+Packed packed_at(char* b, const PackWs& w) {
+  Packed k;
+  k.perm = (int*)(b + w.perm);
+  k.rank = (int*)(b + w.rank);
+  k.N = (int*)(b + w.N);
+  k.Hc = b + w.Hc;
+  k.lse = (float*)(b + w.lse);
+  k.rl = (float*)(b + w.rl);
+  return k;
+}
+
+// The kept rows of `mask`, packed: their positions and ranks, their number
+// (the N of the mean) and the packed copy of their H rows (zero rows after
+// them, up to T).
+hipError_t pack_rows(const Plan& q, const Packed& k, const uint8_t* mask, const void* H, hipStream_t st) {
+  hipError_t e = timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_compact_rows(mask, (int)q.T, k.perm, k.rank, k.N, st); });
+  if (e != hipSuccess) return e;
+  return timed(CKL_KERNEL_OTHER, st,
+               [&] { return ckl::launch_gather_rows(H, (int)q.T, q.d * q.esz, k.perm, k.N, k.Hc, st); });
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -372,7 +448,7 @@ ckl_status ckl_workspace_size(const ckl_problem* p, int which, size_t* bytes) {
     return fail(CKL_ERR_INVALID_ARG,
                 "which must be 0 (forward, shard forward), 1 (backward), 2 (forward + backward) or 3 (shard combine)");
   const Plan q = make_plan(p);
-  *bytes = which == 0   ? fwd_layout(q).total
+  *bytes = which == 0   ? fwd_layout(q, p).total
            : which == 1 ? bwd_layout(q, p).total
            : which == 2 ? fused_layout(q, p).total
                         : combine_layout(q).total;
@@ -392,7 +468,7 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   if (((uintptr_t)loss & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)row_loss & 3u))
     return fail(CKL_ERR_INVALID_ARG, "loss, lse and row_loss must be 4-byte aligned");
   const Plan q = make_plan(p);
-  const FwdWs w = fwd_layout(q);
+  const FwdWs w = fwd_layout(q, p);
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", w.total, ws ? ws_bytes : (size_t)0);
   hipStream_t st = (hipStream_t)stream;
@@ -405,13 +481,27 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   int* N = (int*)(b + w.N);
   int* bad = (int*)(b + w.bad);
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
-
-  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  // packed rows: the kept rows first, everything below runs over them only
+  const Packed pk = (p->compact_mask && mask) ? packed_at(b, w.pk) : Packed{};
+  const void* Hs = H;
+  const uint8_t* mk = mask;
+  float* lse_o = lse;
+  float* rl_o = row_loss;
+  if (pk.on()) {
+    HIP_TRY(pack_rows(q, pk, mask, H, st), "packing kept rows");
+    N = pk.N;
+    Hs = pk.Hc;
+    mk = nullptr;
+    lse_o = pk.lse;
+    rl_o = row_loss ? pk.rl : nullptr;
+  } else {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  }
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, E, M, zg_s,
-                                                  p->validate ? bad : nullptr, p->teacher_form, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, pk.perm, pk.N, st);
                 }),
           "teacher_prep");
   if (p->validate) {
@@ -427,23 +517,31 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
     const int64_t tb0 = c * q.Cs;
     const int rows = (int)std::min(q.Cs, q.T - tb0);
     if (rows <= 0) break;
-    const char* Hc = (const char*)H + tb0 * q.d * q.esz;
+    const char* Hc = (const char*)Hs + tb0 * q.d * q.esz;
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
                     return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
-                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0, st);
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0,
+                                               pk.N, (int)tb0, st);
                   }),
             "fwd_lse");
     HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
                   [&] {
                     return ckl::launch_fwd_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K, zg_s + tb0 * K,
-                                                E + tb0, M + tb0, mask ? mask + tb0 : nullptr, lse + tb0,
-                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0, st);
+                                                E + tb0, M + tb0, mk ? mk + tb0 : nullptr, lse_o + tb0,
+                                                rl_o ? rl_o + tb0 : nullptr, blk + tb0, pk.N, (int)tb0, st);
                   }),
             "fwd_rows");
   }
   HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st, [&] { return ckl::launch_loss_reduce(blk, T, N, loss, st); }),
           "loss_reduce");
+  if (pk.on()) {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_scatter_f32(pk.lse, pk.rank, T, lse, st); }),
+            "scatter lse");
+    if (row_loss)
+      HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_scatter_f32(pk.rl, pk.rank, T, row_loss, st); }),
+              "scatter row loss");
+  }
   return CKL_OK;
 }
 
@@ -478,26 +576,42 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
     Gbuf[i] = b + w.G[i];
     Gtbuf[i] = q.in_bf16 ? nullptr : b + w.Gt[i];
   }
-  float* dHacc = p->dh_dtype == CKL_BF16 ? (float*)(b + w.dH) : (float*)dH;
-  float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
-
-  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  const Packed pk = (p->compact_mask && mask) ? packed_at(b, w.pk) : Packed{};
+  // dH accumulates in fp32: in dH itself, or in the workspace when dH is
+  // bf16 or its rows are packed (scattered back at the end)
+  float* dHacc = (p->dh_dtype == CKL_BF16 || pk.on()) ? (float*)(b + w.dH) : (float*)dH;
+  float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
+  const void* Hs = H;
+  const uint8_t* mk = mask;
+  const float* lse_s = lse;
+  if (pk.on()) {
+    HIP_TRY(pack_rows(q, pk, mask, H, st), "packing kept rows");
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_gather_f32(lse, pk.perm, pk.N, T, pk.lse, st); }),
+            "gather lse");
+    N = pk.N;
+    Hs = pk.Hc;
+    mk = nullptr;
+    lse_s = pk.lse;
+  } else {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  }
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, nullptr, M, nullptr,
-                                                  p->validate ? bad : nullptr, p->teacher_form, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, pk.perm, pk.N, st);
                 }),
           "teacher_prep");
   if (p->validate) {
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st); }),
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                [&] { return ckl::launch_row_scale(mk, grad_loss, N, T, (int)q.Tp, pk.on(), srow, st); }),
           "row_scale");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, q.Tp + kLdPad, st); }),
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, Hs, T, d, (int)q.Tp, Ht, q.Tp + kLdPad, st); }),
           "transpose H");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
                 [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp + kLdPad, st); }),
@@ -517,9 +631,9 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
       pick_splits(trows / q.BN, vrows / q.BM, &splits, &tps);
       HIP_TRY(timed(CKL_KERNEL_BWD_GRAD, st,
                     [&] {
-                      return ckl::launch_bwd_grad(q.in_bf16, H, W, T, d, V, K, idx_s, p_s, M, lse, srow, (int)tb0,
+                      return ckl::launch_bwd_grad(q.in_bf16, Hs, W, T, d, V, K, idx_s, p_s, M, lse_s, srow, (int)tb0,
                                                   (int)trows, (int)vb0, (int)vrows, (int)splits, (int)tps, G,
-                                                  vrows + kLdPad, Gt, trows + kLdPad, st);
+                                                  vrows + kLdPad, Gt, trows + kLdPad, pk.N, st);
                     }),
               "bwd_grad");
       // dW[vb0 .. vb0 + vrows) (+)= G^T H[tb0 .. tb0 + trows)  (longer k: scheduled first)
@@ -528,15 +642,26 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
       ckl::GemmArgs gdw{q.in_bf16 ? G : Gt, q.in_bf16 ? vrows + kLdPad : trows + kLdPad, Htb + tb0 * q.esz,
                         q.Tp + kLdPad, dWacc + vb0 * q.d, q.d, (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
       gdw.xt = q.in_bf16;
-      const ckl::GemmArgs gdh{G, vrows + kLdPad, Wtb + vb0 * q.esz, q.Vp + kLdPad, dHacc + tb0 * q.d, q.d,
-                              (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
+      ckl::GemmArgs gdh{G, vrows + kLdPad, Wtb + vb0 * q.esz, q.Vp + kLdPad, dHacc + tb0 * q.d, q.d,
+                        (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
+      if (pk.on()) {
+        // packed rows: the token rows of this block past the kept rows are
+        // skipped (their G rows were not formed)
+        gdw.lim = pk.N; gdw.lim_base = (int)tb0; gdw.lim_kind = 2; gdw.lim_round = (int)q.BN;
+        gdh.lim = pk.N; gdh.lim_base = (int)tb0; gdh.lim_kind = 1;
+      }
       HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdw, gdh, st); }),
               "gemm dW + dH");
     }
   }
-  if (p->dh_dtype == CKL_BF16)
+  if (pk.on()) {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                  [&] { return ckl::launch_scatter_rows(dHacc, pk.rank, T, d, dH, p->dh_dtype == CKL_BF16, st); }),
+            "scatter dH");
+  } else if (p->dh_dtype == CKL_BF16) {
     HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dHacc, dH, q.T * q.d, st); }),
             "cast dH");
+  }
   if (p->dw_dtype == CKL_BF16)
     HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),
             "cast dW");
@@ -584,23 +709,38 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
   const int64_t ldG = q.Vp + kLdPad, ldGt = q.Gc * q.Cs + kGtPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
-
-  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  const int64_t dh_esz = p->dh_dtype == CKL_BF16 ? 2 : 4;
+  const Packed pk = (p->compact_mask && mask) ? packed_at(b, w.pk) : Packed{};
+  const void* Hs = H;
+  const uint8_t* mk = mask;
+  float* lse_o = lse;
+  float* rl_o = row_loss;
+  if (pk.on()) {
+    HIP_TRY(pack_rows(q, pk, mask, H, st), "packing kept rows");
+    N = pk.N;
+    Hs = pk.Hc;
+    mk = nullptr;
+    lse_o = pk.lse;
+    rl_o = row_loss ? pk.rl : nullptr;
+  } else {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_count_mask(mask, T, N, st); }), "count_mask");
+  }
   if (p->validate) HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_fill_i32(bad, 1, 0, st); }), "fill");
   HIP_TRY(timed(CKL_KERNEL_TEACHER_PREP, st,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s, E, M, zg_s,
-                                                  p->validate ? bad : nullptr, p->teacher_form, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, pk.perm, pk.N, st);
                 }),
           "teacher_prep");
   if (p->validate) {
     s = check_validate_flag(bad, st);
     if (s != CKL_OK) return s;
   }
-  HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_row_scale(mask, grad_loss, N, T, (int)q.Tp, srow, st); }),
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                [&] { return ckl::launch_row_scale(mk, grad_loss, N, T, (int)q.Tp, pk.on(), srow, st); }),
           "row_scale");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, H, T, d, (int)q.Tp, Ht, ldH, st); }),
+                [&] { return ckl::launch_transpose_pad(q.in_bf16, Hs, T, d, (int)q.Tp, Ht, ldH, st); }),
           "transpose H");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
                 [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, ldW, st); }),
@@ -615,34 +755,35 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     char* Gc = q.in_bf16 ? G + slot * q.Cs * ldG * q.esz : G;
     char* Gtc = q.in_bf16 ? nullptr : Gt + slot * q.Cs * q.esz;
     const bool dw_now = slot == q.Gc - 1 || c == q.nS - 1;       // the group's last chunk
-    const char* Hc = (const char*)H + tb0 * q.d * q.esz;
+    const char* Hc = (const char*)Hs + tb0 * q.d * q.esz;
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
                     return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
                                                b + w.part, (int)q.c_splits, (int)q.c_tps, q.in_bf16 ? U : G, ldG,
-                                               mtab, q.Cs, st);
+                                               mtab, q.Cs, pk.N, (int)tb0, st);
                   }),
             "fwd_lse (store)");
     HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
                   [&] {
                     return ckl::launch_fwd_rows(b + w.part, (int)q.c_splits, rows, K, p_s + tb0 * K, zg_s + tb0 * K,
-                                                E + tb0, M + tb0, mask ? mask + tb0 : nullptr, lse + tb0,
-                                                row_loss ? row_loss + tb0 : nullptr, blk + tb0, st);
+                                                E + tb0, M + tb0, mk ? mk + tb0 : nullptr, lse_o + tb0,
+                                                rl_o ? rl_o + tb0 : nullptr, blk + tb0, pk.N, (int)tb0, st);
                   }),
             "fwd_rows");
     HIP_TRY(timed(CKL_KERNEL_G_PASS, st,
                   [&] {
                     if (q.in_bf16)
                       return ckl::launch_gpass_tiles(U, (int)(q.Vp / q.BM), rows_p / (int)q.BN, Gc, ldG, Gtc, ldGt,
-                                                     mtab, q.Cs, srow + tb0, M + tb0, lse + tb0, rows, V, st);
-                    return ckl::launch_gpass(q.in_bf16, G, ldG, Gtc, ldGt, mtab, q.Cs, srow + tb0, M + tb0, lse + tb0,
-                                             rows, rows_p, V, (int)q.Vp, st);
+                                                     mtab, q.Cs, srow + tb0, M + tb0, lse_o + tb0, rows, V, pk.N,
+                                                     (int)tb0, st);
+                    return ckl::launch_gpass(q.in_bf16, G, ldG, Gtc, ldGt, mtab, q.Cs, srow + tb0, M + tb0,
+                                             lse_o + tb0, rows, rows_p, V, (int)q.Vp, st);
                   }),
             "gpass");
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,
                   [&] {
                     return ckl::launch_gfix(q.in_bf16, rows, K, V, idx_s + tb0 * K, p_s + tb0 * K, zg_s + tb0 * K,
-                                            srow + tb0, M + tb0, lse + tb0, Gc, ldG, Gtc, ldGt, st);
+                                            srow + tb0, M + tb0, lse_o + tb0, Gc, ldG, Gtc, ldGt, st);
                   }),
             "gfix");
     // dH rows of the chunk as Sh split-k partials (long k: scheduled first);
@@ -659,19 +800,37 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     ckl::GemmArgs gdw{q.in_bf16 ? (void*)G : (void*)Gt, q.in_bf16 ? ldG : ldGt, Ht + g0 * q.Cs * q.esz, ldH,
                       dWacc, q.d, dw_now ? V : 0, d, (int)(slot * q.Cs + rows_p), g0 > 0};
     gdw.xt = q.in_bf16;
+    if (pk.on()) {
+      // packed rows: rows past the kept rows are skipped (no G formed for
+      // their tiles)
+      gdh.lim = pk.N; gdh.lim_base = (int)tb0; gdh.lim_kind = 1;
+      gdw.lim = pk.N; gdw.lim_base = (int)(g0 * q.Cs); gdw.lim_kind = 2; gdw.lim_round = (int)q.BN;
+    }
     HIP_TRY(timed(CKL_KERNEL_GEMM_DHDW, st, [&] { return ckl::launch_gemm_pair(q.in_bf16, gdh, gdw, st); }),
             "gemm dH parts + dW");
     HIP_TRY(timed(CKL_KERNEL_OTHER, st,
                   [&] {
+                    if (pk.on())
+                      return ckl::launch_splitk_sum(dHp, q.Cs * q.d, (int)q.Sh, (int64_t)rows * q.d, dH,
+                                                    p->dh_dtype == CKL_BF16, pk.perm + tb0, pk.N, (int)tb0, d, st);
                     return ckl::launch_splitk_sum(dHp, q.Cs * q.d, (int)q.Sh, (int64_t)rows * q.d,
-                                                  (char*)dH + tb0 * q.d * (p->dh_dtype == CKL_BF16 ? 2 : 4),
-                                                  p->dh_dtype == CKL_BF16, st);
+                                                  (char*)dH + tb0 * q.d * dh_esz, p->dh_dtype == CKL_BF16, nullptr,
+                                                  nullptr, 0, d, st);
                   }),
             "dH sum");
   }
   HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
                 [&] { return ckl::launch_loss_reduce(blk, (int)q.T, N, loss, st); }),
           "loss_reduce");
+  if (pk.on()) {
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_zero_masked_rows(pk.rank, T, q.d * dh_esz, dH, st); }),
+            "zero masked dH rows");
+    HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_scatter_f32(pk.lse, pk.rank, T, lse, st); }),
+            "scatter lse");
+    if (row_loss)
+      HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_scatter_f32(pk.rl, pk.rank, T, row_loss, st); }),
+              "scatter row loss");
+  }
   if (p->dw_dtype == CKL_BF16)
     HIP_TRY(timed(CKL_KERNEL_OTHER, st, [&] { return ckl::launch_cast_f32_bf16(dWacc, dW, q.V * q.d, st); }),
             "cast dW");
@@ -690,7 +849,7 @@ ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
   if (((uintptr_t)lse_part & 3u) || ((uintptr_t)cross_part & 3u))
     return fail(CKL_ERR_INVALID_ARG, "lse_part and cross_part must be 4-byte aligned");
   const Plan q = make_plan(p);
-  const FwdWs w = fwd_layout(q);
+  const FwdWs w = fwd_layout(q, p);
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "shard forward workspace needs %zu bytes, got %zu", w.total,
                 ws ? ws_bytes : (size_t)0);
@@ -706,7 +865,7 @@ ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), (int)p->v_offset, idx_s, p_s,
                                                   (float*)(b + w.E), (float*)(b + w.M), zg_s,
-                                                  p->validate ? bad : nullptr, p->teacher_form, st);
+                                                  p->validate ? bad : nullptr, p->teacher_form, nullptr, nullptr, st);
                 }),
           "teacher_prep");
   if (p->validate) {
@@ -722,7 +881,8 @@ ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
                     return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
-                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0, st);
+                                               b + w.part, (int)q.c_splits, (int)q.c_tps, nullptr, 0, nullptr, 0,
+                                               nullptr, 0, st);
                   }),
             "fwd_lse");
     HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
@@ -762,7 +922,7 @@ ckl_status ckl_shard_combine(const ckl_problem* p, int32_t n_shards, const float
                 [&] {
                   return ckl::launch_teacher_prep(idx, tlogit, T, K, (int)vtotal(p), 0, (int*)(b + w.idx_s),
                                                   (float*)(b + w.p_s), (float*)(b + w.E), (float*)(b + w.M), nullptr,
-                                                  nullptr, p->teacher_form, st);
+                                                  nullptr, p->teacher_form, nullptr, nullptr, st);
                 }),
           "teacher_prep");
   HIP_TRY(timed(CKL_KERNEL_FWD_FINALIZE, st,
@@ -775,7 +935,7 @@ ckl_status ckl_shard_combine(const ckl_problem* p, int32_t n_shards, const float
   return CKL_OK;
 }
 
-ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]) {
+ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[5]) {
   ckl_status s = check_problem(p);
   if (s != CKL_OK) return s;
   if (!out) return fail(CKL_ERR_INVALID_ARG, "out is NULL");
@@ -784,6 +944,24 @@ ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]) {
   out[1] = q.nS;
   out[2] = q.Sh;
   out[3] = q.Vs;
+  out[4] = q.Gc;
+  return CKL_OK;
+}
+
+ckl_status ckl_scale_cast(const float* src, void* dst, int64_t n, int32_t dst_dtype, const float* scale,
+                          void* stream) {
+  if (!src || !dst) return fail(CKL_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if (n < 0 || n % 4) return fail(CKL_ERR_INVALID_ARG, "n=%lld must be a non-negative multiple of 4", (long long)n);
+  if (dst_dtype != CKL_F32 && dst_dtype != CKL_BF16)
+    return fail(CKL_ERR_INVALID_ARG, "dst_dtype must be CKL_F32 (0) or CKL_BF16 (1)");
+  if (!aligned16(src) || !aligned16(dst)) return fail(CKL_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if ((uintptr_t)scale & 3u) return fail(CKL_ERR_INVALID_ARG, "scale must be 4-byte aligned");
+  if (dst_dtype == CKL_BF16 && (const char*)dst < (const char*)(src + n) && (const char*)src < (const char*)dst + n * 2)
+    return fail(CKL_ERR_INVALID_ARG, "a bf16 dst must not overlap src");
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(timed(CKL_KERNEL_OTHER, st,
+                [&] { return ckl::launch_scale_cast(src, dst, n, dst_dtype == CKL_BF16, scale, st); }),
+          "scale_cast");
   return CKL_OK;
 }
 
@@ -837,6 +1015,6 @@ const char* ckl_status_string(ckl_status s) {
 
 const char* ckl_last_error(void) { return g_last_error.c_str(); }
 
-int32_t ckl_version(void) { return (1 << 16) | 2; }
+int32_t ckl_version(void) { return (2 << 16) | 0; }
 
 }  // extern "C"

@@ -110,33 +110,161 @@ __global__ __launch_bounds__(1024) void count_mask_kernel(const uint8_t* __restr
   if (threadIdx.x == 0) *N = red[0];
 }
 
-// s[t] = grad_loss * keep_t / N for t < T, 0 for T <= t < Tp.
+// s[t] = grad_loss * keep_t / N for t < T, 0 for T <= t < Tp.  Packed rows
+// (mask NULL, N kept rows first): keep_t = t < N.
 __global__ void row_scale_kernel(const uint8_t* __restrict__ mask, const float* __restrict__ grad_loss,
-                                 const int* __restrict__ N, int T, int Tp, float* __restrict__ s) {
+                                 const int* __restrict__ N, int T, int Tp, int packed, float* __restrict__ s) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= Tp) return;
   const int n = *N;
   const float g = grad_loss ? *grad_loss : 1.f;
   float v = 0.f;
-  if (t < T && n > 0 && (mask == nullptr || mask[t] != 0)) v = g / (float)n;
+  if (t < T && n > 0 && (mask == nullptr || mask[t] != 0) && (!packed || t < n)) v = g / (float)n;
   s[t] = v;
+}
+
+// ------------------------------------------------------- packed rows --
+// The kept rows of a mask, in ascending order: perm[i] (i < N) is the i-th
+// kept row, rank[t] its position among them (-1 for a masked row), *N their
+// number.  One workgroup; thread j scans rows [j seg, (j + 1) seg), the
+// counts of the segments are scanned in LDS.
+__global__ __launch_bounds__(1024) void compact_rows_kernel(const uint8_t* __restrict__ mask, int T,
+                                                            int* __restrict__ perm, int* __restrict__ rank,
+                                                            int* __restrict__ N) {
+  __shared__ int cnt[1024];
+  const int seg = (T + 1023) / 1024;
+  const int a = min(T, (int)threadIdx.x * seg), b = min(T, a + seg);
+  int c = 0;
+  for (int t = a; t < b; ++t) c += mask[t] != 0;
+  cnt[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+    const int v = threadIdx.x >= (unsigned)o ? cnt[threadIdx.x - o] : 0;
+    __syncthreads();
+    cnt[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int pos = cnt[threadIdx.x] - c;
+  for (int t = a; t < b; ++t) {
+    if (mask[t] != 0) {
+      perm[pos] = t;
+      rank[t] = pos++;
+    } else {
+      rank[t] = -1;
+    }
+  }
+  if (threadIdx.x == 1023) *N = cnt[1023];
+}
+
+// dst row i = src row perm[i] for i < *N, zeros for *N <= i < rows; rows of
+// `chunks` 16-byte pieces.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ src, int64_t chunks,
+                                                          const int* __restrict__ perm, const int* __restrict__ N,
+                                                          int rows, u32x4* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * chunks) return;
+  const int r = (int)(i / chunks);
+  const int64_t c = i - (int64_t)r * chunks;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (r < *N) v = src[(int64_t)perm[r] * chunks + c];
+  dst[i] = v;
+}
+
+// dst[i] = src[perm[i]] for i < *N, 0 for *N <= i < rows.
+__global__ __launch_bounds__(256) void gather_f32_kernel(const float* __restrict__ src, const int* __restrict__ perm,
+                                                         const int* __restrict__ N, int rows, float* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows) return;
+  dst[i] = i < *N ? src[perm[i]] : 0.f;
+}
+
+// dst[t] = src[rank[t]] for kept rows, 0 for masked rows (rank -1).
+__global__ __launch_bounds__(256) void scatter_f32_kernel(const float* __restrict__ src, const int* __restrict__ rank,
+                                                          int T, float* __restrict__ dst) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int r = rank[t];
+  dst[t] = r >= 0 ? src[r] : 0.f;
+}
+
+// dst row t (d elements, fp32 or bf16) = packed fp32 row rank[t], or zeros
+// for a masked row; four elements per thread.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restrict__ src, const int* __restrict__ rank,
+                                                           int T, int d, void* __restrict__ dst, int dst_bf16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = d / 4;
+  if (i >= (int64_t)T * q) return;
+  const int t = (int)(i / q);
+  const int c = (int)(i - (int64_t)t * q);
+  const int r = rank[t];
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  if (r >= 0) a = reinterpret_cast<const f32x4*>(src + (int64_t)r * d)[c];
+  if (dst_bf16)
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(dst) + (int64_t)t * d + 4 * c) =
+        u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+  else
+    reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + (int64_t)t * d)[c] = a;
+}
+
+// Rows t of dst (`chunks` 16-byte pieces each) with rank[t] < 0 set to zero.
+__global__ __launch_bounds__(256) void zero_masked_rows_kernel(const int* __restrict__ rank, int T, int64_t chunks,
+                                                               u32x4* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * chunks) return;
+  const int t = (int)(i / chunks);
+  if (rank[t] < 0) dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// dst[i] = scale * src[i], rounded once to dst's type; four per thread.
+// (src and dst may be the same fp32 array: each element is read before the
+// same thread overwrites it)
+__global__ __launch_bounds__(256) void scale_cast_kernel(const float* src, void* dst, int64_t n4, int dst_bf16,
+                                                         const float* __restrict__ scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float g = scale ? *scale : 1.f;
+  const f32x4 a = reinterpret_cast<const f32x4*>(src)[i] * g;
+  if (dst_bf16)
+    reinterpret_cast<u32x2*>(dst)[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+  else
+    reinterpret_cast<f32x4*>(dst)[i] = a;
 }
 
 // One wavefront per row.  Softmax of the K cached logits (fp32), then a
 // bitonic sort of (idx, p) by idx in LDS.  Optional outputs: E (sum p log p),
-// zero-filled zg.  `bad` collects out-of-range / repeated indices.
+// zero-filled zg.  `bad` collects out-of-range / repeated indices.  Packed
+// rows (rowmap not NULL): row t takes the teacher of row rowmap[t] for
+// t < *nrows; rows past *nrows get an empty teacher (no index, p = E = M = 0).
 __global__ __launch_bounds__(64) void teacher_prep_kernel(const int* __restrict__ idx, const float* __restrict__ tlogit,
                                                           int T, int K, int Kp, int V, int voff, int* __restrict__ idx_s,
                                                           float* __restrict__ p_s, float* __restrict__ Erow,
                                                           float* __restrict__ Mrow, float* __restrict__ zg_s,
-                                                          int* __restrict__ bad, int logprob) {
+                                                          int* __restrict__ bad, int logprob,
+                                                          const int* __restrict__ rowmap,
+                                                          const int* __restrict__ nrows) {
   extern __shared__ int sm_dyn[];
   int* key = sm_dyn;
   float* val = reinterpret_cast<float*>(sm_dyn + Kp);
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  const int* irow = idx + (int64_t)t * K;
-  const float* lrow = tlogit + (int64_t)t * K;
+  int src = t;
+  if (rowmap != nullptr) {
+    if (t >= *nrows) {
+      for (int k = lane; k < K; k += 64) {
+        idx_s[(int64_t)t * K + k] = kIdxEnd;
+        p_s[(int64_t)t * K + k] = 0.f;
+        if (zg_s) zg_s[(int64_t)t * K + k] = 0.f;
+      }
+      if (lane == 0) {
+        if (Erow) Erow[t] = 0.f;
+        Mrow[t] = 0.f;
+      }
+      return;
+    }
+    src = rowmap[t];
+  }
+  const int* irow = idx + (int64_t)src * K;
+  const float* lrow = tlogit + (int64_t)src * K;
 
   // logits: p = softmax over the K entries (shifted by the row maximum);
   // log-probabilities: p = exp(entry) as given (mass M may be below one)
@@ -220,7 +348,7 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
     const int* __restrict__ idx_s, float* __restrict__ zg_s, float2* __restrict__ part, int n_vtiles,
     int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
-    float* __restrict__ mtab, int64_t ldm) {
+    float* __restrict__ mtab, int64_t ldm, const int* __restrict__ nrows, int row0) {
   using TIn = typename C::TIn;
   using TileT = typename C::TileT;
   using L = typename TileT::L;
@@ -247,6 +375,10 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   int tblock, split;
   grouped_mn(xcd_remap(blockIdx.x, n_tblocks * n_splits), n_tblocks, n_splits, kGroupT, tblock, split);
   const int t0 = tblock * C::BN;
+  // packed rows: only the first *nrows - row0 rows of this call hold kept
+  // rows (the rest are zero rows); whole token blocks past them are skipped
+  // (their split states, u and maxima are never read)
+  if (nrows != nullptr && t0 >= *nrows - row0) return;
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
   const int own_nb = lane / GLANES;
@@ -441,6 +573,8 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
 // M_t LSE, and l_t in fp64 at row_ld[t] for the deterministic mean (0 for
 // masked rows).  Lane j of a row takes splits j, j + 16, .. and teacher
 // entries j, j + 16, ..; the partials merge by shuffles in a fixed order.
+// Packed rows (nrows not NULL): rows t >= *nrows - row0 are padding, treated
+// as masked.
 __global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restrict__ part, int S, int T, int K,
                                                            const float* __restrict__ p_s,
                                                            const float* __restrict__ zg_s,
@@ -449,11 +583,13 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(const float2* __restr
                                                            const uint8_t* __restrict__ mask,
                                                            float* __restrict__ lse_out,
                                                            float* __restrict__ row_loss,
-                                                           double* __restrict__ row_ld) {
+                                                           double* __restrict__ row_ld,
+                                                           const int* __restrict__ nrows, int row0) {
   const int sub = threadIdx.x & 15;
   const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   const bool valid = t < T;
-  const bool keep = valid && (mask == nullptr || mask[t] != 0);
+  const bool keep =
+      valid && (mask == nullptr || mask[t] != 0) && (nrows == nullptr || t < *nrows - row0);
   float m = -INFINITY, s = 0.f;
   double x = 0.0;
   if (keep) {
@@ -648,7 +784,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
     const int* __restrict__ idx_s, const float* __restrict__ p_s, const float* __restrict__ Mrow,
     const float* __restrict__ lse, const float* __restrict__ srow, int tb0, int vb0, int n_vtiles,
     int tiles_per_split, int n_tblocks, int n_splits, typename C::TIn* __restrict__ G, int64_t ldG,
-    typename C::TIn* __restrict__ Gt, int64_t ldGt) {
+    typename C::TIn* __restrict__ Gt, int64_t ldGt, const int* __restrict__ nrows) {
   using TIn = typename C::TIn;
   // bf16 256 x 256 tiles leave the kernel through the LDS (the whole tile,
   // 128 KiB, once the main loop is done with it) as 16-byte stores that
@@ -671,6 +807,9 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   int tblock, split;
   grouped_mn(xcd_remap(blockIdx.x, n_tblocks * n_splits), n_tblocks, n_splits, kGroupT, tblock, split);
   const int t0 = tb0 + tblock * C::BN;
+  // packed rows: token blocks wholly past the kept rows are skipped (the
+  // contractions read no G row of them)
+  if (nrows != nullptr && t0 >= *nrows) return;
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
 
@@ -923,7 +1062,8 @@ __global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __r
                                                                const float* __restrict__ mtab, int64_t ldm,
                                                                const float* __restrict__ srow,
                                                                const float* __restrict__ Mrow,
-                                                               const float* __restrict__ lse, int rows, int V) {
+                                                               const float* __restrict__ lse, int rows, int V,
+                                                               const int* __restrict__ nrows, int row0) {
   using C = CfgBF16;
   static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128 && C::WN == 64 && C::MB == 4 && C::NB == 2 &&
                     C::WAVES_M == 2 && C::WAVES_N == 4,
@@ -936,6 +1076,9 @@ __global__ __launch_bounds__(256 * TH) void gpass_tiles_kernel(const bf16_t* __r
   __shared__ float fs[2][TR];  // g / u per (wave_m, token): s_t M_t 2^(m - LSE_t log2e), 0 for no gradient
   const int vt = blockIdx.x, tb = blockIdx.y / (4 / TH), th = blockIdx.y % (4 / TH);
   const int t0 = tb * 256 + th * TR, v0 = vt * 256;
+  // packed rows: whole 256-row tiles past the kept rows are skipped (the
+  // forward kept no u for them; the contractions read none of their rows)
+  if (nrows != nullptr && tb * 256 >= *nrows - row0) return;
   const int tid = threadIdx.x;
   const u32x4* ut = reinterpret_cast<const u32x4*>(U + ((int64_t)tb * n_vtiles + vt) * (256 * 256));
   auto phys = [](int t, int c) { return c ^ ((t >> 3) & 31); };
@@ -1042,16 +1185,27 @@ __global__ __launch_bounds__(256) void gfix_kernel(int rows, int K, int V, const
 }
 
 // out[i] = part[i] + part[pstride + i] + ... (S terms, this order), 4 per thread.
+// Packed rows (rowmap not NULL, rows of d elements): row r of the sum goes to
+// row rowmap[r] of out, for r < *nrows - row0 only.
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int64_t pstride, int S,
-                                                         int64_t n4, void* __restrict__ out, int out_bf16) {
+                                                         int64_t n4, void* __restrict__ out, int out_bf16,
+                                                         const int* __restrict__ rowmap, const int* __restrict__ nrows,
+                                                         int row0, int d) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
+  int64_t o = i;
+  if (rowmap != nullptr) {
+    const int q = d / 4;
+    const int r = (int)(i / q);
+    if (r >= *nrows - row0) return;
+    o = (int64_t)rowmap[r] * q + (i - (int64_t)r * q);
+  }
   f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
   for (int s = 1; s < S; ++s) a += reinterpret_cast<const f32x4*>(part + s * pstride)[i];
   if (out_bf16)
-    store4<bf16_t>(reinterpret_cast<bf16_t*>(out) + 4 * i, a[0], a[1], a[2], a[3]);
+    store4<bf16_t>(reinterpret_cast<bf16_t*>(out) + 4 * o, a[0], a[1], a[2], a[3]);
   else
-    reinterpret_cast<f32x4*>(out)[i] = a;
+    reinterpret_cast<f32x4*>(out)[o] = a;
 }
 
 // ------------------------------------------------------ plain contraction --
@@ -1078,6 +1232,10 @@ struct GemmProblem {
   int64_t xb, yb, ob;
   int xt;              // X k-major (Dma64 configurations with the substep pipeline)
   int tiles_m, tiles;  // tiles_m = ceil(M / BM); tiles = tiles_m * ceil(N / BN) * batches
+  // packed rows: lim_kind 1 bounds M, 2 bounds kdim, by *lim - lim_base
+  // (kdim rounded up to lim_round, the rows of whole G tiles)
+  const int* lim;
+  int lim_base, lim_kind, lim_round;
 };
 
 constexpr int kGroupM = 2;
@@ -1131,20 +1289,40 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
     Y += bt * (second ? p1.yb : p0.yb);
     out += bt * (second ? p1.ob : p0.ob);
   }
-  const int kdim = bt == batches - 1 ? (second ? p1.kdim_last : p0.kdim_last) : kdim_all;
+  int kdim = bt == batches - 1 ? (second ? p1.kdim_last : p0.kdim_last) : kdim_all;
   int tm, tn;
   grouped_mn(bid, tiles_m, per_batch / tiles_m, kGroupM, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
+  // packed rows: tiles past the kept rows are skipped, contractions over
+  // token rows stop after them (a skipped k range adds nothing: with beta the
+  // tile is left as it is, without it the zero tile is still written)
+  int M_eff = M;
+  {
+    const int* lim = second ? p1.lim : p0.lim;
+    if (lim != nullptr) {
+      const int kind = second ? p1.lim_kind : p0.lim_kind;
+      const int n_lim = *lim - (second ? p1.lim_base : p0.lim_base);
+      if (kind == 1) {
+        M_eff = max(0, min(M, n_lim));
+        if (m0 >= M_eff) return;
+      } else if (kind == 2) {
+        const int rnd = second ? p1.lim_round : p0.lim_round;
+        const int kl = n_lim <= 0 ? 0 : (n_lim + rnd - 1) / rnd * rnd;
+        kdim = min(kdim, kl);
+        if (kdim <= 0 && beta) return;
+      }
+    }
+  }
   using TileT = typename C::TileT;
   using L = typename TileT::L;
   TileT tile;
   if constexpr (kXtOK<C>) {
     if (second ? p1.xt : p0.xt)
-      run_mma<C, false, true>(tile, X + m0, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+      run_mma<C, false, true>(tile, X + m0, ldx, M_eff - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
     else
-      run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+      run_mma(tile, X + (int64_t)m0 * ldx, ldx, M_eff - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
   } else {
-    run_mma(tile, X + (int64_t)m0 * ldx, ldx, M - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
+    run_mma(tile, X + (int64_t)m0 * ldx, ldx, M_eff - m0, Y + (int64_t)n0 * ldy, ldy, N - n0, kdim, smem);
   }
   if constexpr (C::WM * C::BN * 4 <= C::LDS_BYTES) {
     // The fp32 tile goes out through LDS, the WM rows of one wave_m at a
@@ -1173,9 +1351,9 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
 #pragma unroll 1
         for (int part = 0; part < C::WAVES_M; ++part) {
           const int r0 = m0 + part * PART;
-          if (beta && r0 < M) {
+          if (beta && r0 < M_eff) {
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(out + (int64_t)r0 * ldo, (uint32_t)(min(M - r0, PART) * ldo * 4));
+                make_rsrc(out + (int64_t)r0 * ldo, (uint32_t)(min(M_eff - r0, PART) * ldo * 4));
 #pragma unroll
             for (int k = 0; k < NLD; ++k) {
               const int q = (k * C::NWAVES + wave) * 64 + lane;
@@ -1203,7 +1381,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
           for (int i = threadIdx.x; i < PART * CPR; i += C::NTHREADS) {
             const int ml = i / CPR, c4 = (i % CPR) * 4;
             const int m = r0 + ml, n = n0 + c4;
-            if (m >= M || n >= N) continue;
+            if (m >= M_eff || n >= N) continue;
             const f32x4 a = *reinterpret_cast<const f32x4*>(st + ml * C::BN + (c4 ^ stage_swz(ml)));
             float* o = out + (int64_t)m * ldo + n;
             if (n + 4 <= N) {
@@ -1249,7 +1427,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
         const int m = m0 + part * PART + ml, n = n0 + c4;
         old[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (beta && vec_ok && m < M && n + 4 <= N)
+        if (beta && vec_ok && m < M_eff && n + 4 <= N)
           old[jj] = *reinterpret_cast<const f32x4*>(out + (int64_t)m * ldo + n);
       }
 #pragma unroll
@@ -1258,7 +1436,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
         const int i = threadIdx.x + (j0 + jj) * C::NTHREADS;
         const int ml = i / (C::BN / 4), c4 = (i % (C::BN / 4)) * 4;
         const int m = m0 + part * PART + ml, n = n0 + c4;
-        if (m >= M || n >= N) continue;
+        if (m >= M_eff || n >= N) continue;
         const float* sv = st + ml * C::BN + (c4 ^ stage_swz(ml));
         float* o = out + (int64_t)m * ldo + n;
         if (vec_ok && n + 4 <= N) {
@@ -1279,7 +1457,7 @@ __global__ __launch_bounds__(C::NTHREADS) void gemm_store_kernel(GemmProblem<typ
 #pragma unroll
         for (int r = 0; r < L::RPB; ++r) {
           const int m = m0 + wave_m * C::WM + mb * L::BLK + L::row_in(r, lane);
-          if (m < M && n < N) {
+          if (m < M_eff && n < N) {
             float* o = out + (int64_t)m * ldo + n;
             const float a = tile.acc[mb][nb][r];
             *o = beta ? *o + a : a;
@@ -1323,21 +1501,84 @@ hipError_t launch_count_mask(const uint8_t* mask, int T, int* N, hipStream_t st)
   return hipSuccess;
 }
 
-hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const int* N, int T, int Tp, float* s,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(row_scale_kernel, dim3((Tp + 255) / 256), dim3(256), 0, st, mask, grad_loss, N, T, Tp, s);
+hipError_t launch_row_scale(const uint8_t* mask, const float* grad_loss, const int* N, int T, int Tp, int packed,
+                            float* s, hipStream_t st) {
+  hipLaunchKernelGGL(row_scale_kernel, dim3((Tp + 255) / 256), dim3(256), 0, st, mask, grad_loss, N, T, Tp, packed, s);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_compact_rows(const uint8_t* mask, int T, int* perm, int* rank, int* N, hipStream_t st) {
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, mask, T, perm, rank, N);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gather_rows(const void* src, int rows, int64_t row_bytes, const int* perm, const int* N, void* dst,
+                              hipStream_t st) {
+  if (row_bytes % 16) return hipErrorInvalidValue;
+  const int64_t chunks = row_bytes / 16, n = (int64_t)rows * chunks;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const u32x4*)src,
+                     chunks, perm, N, rows, (u32x4*)dst);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gather_f32(const float* src, const int* perm, const int* N, int rows, float* dst, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_f32_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, src, perm, N, rows, dst);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_scatter_f32(const float* src, const int* rank, int T, float* dst, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_f32_kernel, dim3((T + 255) / 256), dim3(256), 0, st, src, rank, T, dst);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_scatter_rows(const float* src, const int* rank, int T, int d, void* dst, int dst_bf16,
+                               hipStream_t st) {
+  if (d % 4) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)T * (d / 4);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, rank, T, d, dst,
+                     dst_bf16);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_zero_masked_rows(const int* rank, int T, int64_t row_bytes, void* dst, hipStream_t st) {
+  if (row_bytes % 16) return hipErrorInvalidValue;
+  const int64_t chunks = row_bytes / 16, n = (int64_t)T * chunks;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_masked_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rank, T, chunks,
+                     (u32x4*)dst);
+  CKL_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_scale_cast(const float* src, void* dst, int64_t n, int dst_bf16, const float* scale,
+                             hipStream_t st) {
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_cast_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, src, dst, n4, dst_bf16,
+                     scale);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
 hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K, int V, int voff, int* idx_s,
                                float* p_s, float* Erow, float* Mrow, float* zg_s, int* bad, int logprob,
-                               hipStream_t st) {
+                               const int* rowmap, const int* nrows, hipStream_t st) {
   int Kp = 64;
   while (Kp < K) Kp <<= 1;
   const size_t lds = (size_t)Kp * 8;
   hipLaunchKernelGGL(teacher_prep_kernel, dim3(T), dim3(64), lds, st, idx, tlogit, T, K, Kp, V, voff, idx_s, p_s,
-                     Erow, Mrow, zg_s, bad, logprob);
+                     Erow, Mrow, zg_s, bad, logprob, rowmap, nrows);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -1345,38 +1586,38 @@ hipError_t launch_teacher_prep(const int* idx, const float* tlogit, int T, int K
 template <typename TIn>
 static hipError_t fwd_lse_t(const void* H, const void* W, int T, int d, int V, int K, const int* idx_s, float* zg_s,
                             void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG, float* mtab,
-                            int64_t ldm, hipStream_t st) {
+                            int64_t ldm, const int* nrows, int row0, hipStream_t st) {
   using C = typename CfgOf<TIn>::type;
   const int n_vtiles = (V + C::BM - 1) / C::BM;
   const int n_tblocks = (T + C::BN - 1) / C::BN;
   if (G)
     hipLaunchKernelGGL((fwd_lse_kernel<C, true>), dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st,
                        (const TIn*)H, (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles,
-                       tiles_per_split, n_tblocks, n_splits, (TIn*)G, ldG, mtab, ldm);
+                       tiles_per_split, n_tblocks, n_splits, (TIn*)G, ldG, mtab, ldm, nrows, row0);
   else
     hipLaunchKernelGGL((fwd_lse_kernel<C, false>), dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st,
                        (const TIn*)H, (const TIn*)W, T, d, V, K, idx_s, zg_s, (float2*)part, n_vtiles,
                        tiles_per_split, n_tblocks, n_splits, (TIn*)nullptr, (int64_t)0, (float*)nullptr,
-                       (int64_t)0);
+                       (int64_t)0, nrows, row0);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
 
 hipError_t launch_fwd_lse(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
                           float* zg_s, void* part, int n_splits, int tiles_per_split, void* G, int64_t ldG,
-                          float* mtab, int64_t ldm, hipStream_t st) {
+                          float* mtab, int64_t ldm, const int* nrows, int row0, hipStream_t st) {
   return in_bf16 ? fwd_lse_t<bf16_t>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, G, ldG, mtab,
-                                     ldm, st)
+                                     ldm, nrows, row0, st)
                  : fwd_lse_t<float>(H, W, T, d, V, K, idx_s, zg_s, part, n_splits, tiles_per_split, G, ldG, mtab,
-                                    ldm, st);
+                                    ldm, nrows, row0, st);
 }
 
 hipError_t launch_fwd_rows(const void* part, int S, int T, int K, const float* p_s, const float* zg_s,
                            const float* Erow, const float* Mrow, const uint8_t* mask, float* lse, float* row_loss,
-                           double* row_ld, hipStream_t st) {
+                           double* row_ld, const int* nrows, int row0, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(fwd_finalize_kernel, dim3((T + 15) / 16), dim3(256), 0, st, (const float2*)part, S, T, K, p_s,
-                     zg_s, Erow, Mrow, mask, lse, row_loss, row_ld);
+                     zg_s, Erow, Mrow, mask, lse, row_loss, row_ld, nrows, row0);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -1435,13 +1676,13 @@ template <typename TIn>
 static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
                              const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
                              int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G,
-                             int64_t ldG, void* Gt, int64_t ldGt, hipStream_t st) {
+                             int64_t ldG, void* Gt, int64_t ldGt, const int* nrows, hipStream_t st) {
   using C = typename CfgOf<TIn>::bwd;
   const int n_vtiles = v_rows / C::BM;
   const int n_tblocks = t_rows / C::BN;
   hipLaunchKernelGGL(bwd_grad_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,
                      (const TIn*)W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, vb0, n_vtiles, tiles_per_split,
-                     n_tblocks, n_splits, (TIn*)G, ldG, (TIn*)Gt, ldGt);
+                     n_tblocks, n_splits, (TIn*)G, ldG, (TIn*)Gt, ldGt, nrows);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -1449,11 +1690,11 @@ static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, 
 hipError_t launch_bwd_grad(int in_bf16, const void* H, const void* W, int T, int d, int V, int K, const int* idx_s,
                            const float* p_s, const float* Mrow, const float* lse, const float* srow, int tb0,
                            int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G, int64_t ldG,
-                           void* Gt, int64_t ldGt, hipStream_t st) {
+                           void* Gt, int64_t ldGt, const int* nrows, hipStream_t st) {
   return in_bf16 ? bwd_grad_t<bf16_t>(H, W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, t_rows, vb0, v_rows,
-                                      n_splits, tiles_per_split, G, ldG, Gt, ldGt, st)
+                                      n_splits, tiles_per_split, G, ldG, Gt, ldGt, nrows, st)
                  : bwd_grad_t<float>(H, W, T, d, V, K, idx_s, p_s, Mrow, lse, srow, tb0, t_rows, vb0, v_rows,
-                                     n_splits, tiles_per_split, G, ldG, Gt, ldGt, st);
+                                     n_splits, tiles_per_split, G, ldG, Gt, ldGt, nrows, st);
 }
 
 template <typename TIn>
@@ -1478,6 +1719,12 @@ static hipError_t gemm_pair_t(const GemmArgs& a0, const GemmArgs& a1, hipStream_
     p[i].yb = a[i]->yb;
     p[i].ob = a[i]->ob;
     p[i].xt = a[i]->xt;
+    p[i].lim = a[i]->lim;
+    p[i].lim_base = a[i]->lim_base;
+    p[i].lim_kind = a[i]->lim ? a[i]->lim_kind : 0;
+    p[i].lim_round = a[i]->lim_round > 0 ? a[i]->lim_round : 1;
+    if (a[i]->lim && (a[i]->lim_kind < 1 || a[i]->lim_kind > 2 || (a[i]->lim_kind == 2 && a[i]->lim_round % 8)))
+      return hipErrorInvalidValue;
     // k-major X: every tile reads BM whole columns of each k row
     if (a[i]->xt && (!kXtOK<C> || a[i]->batches > 1 || (int64_t)(a[i]->M + C::BM - 1) / C::BM * C::BM > a[i]->ldx))
       return hipErrorInvalidValue;
@@ -1511,11 +1758,11 @@ constexpr int kGpassTH = 2;  // forward wave columns (64 tokens each) per G-form
 
 hipError_t launch_gpass_tiles(const void* U, int n_vtiles, int n_tblocks, void* G, int64_t ldG, void* Gt,
                               int64_t ldGt, const float* mtab, int64_t ldm, const float* srow, const float* Mrow,
-                              const float* lse, int rows, int V, hipStream_t st) {
+                              const float* lse, int rows, int V, const int* nrows, int row0, hipStream_t st) {
   if (n_vtiles < 1 || n_tblocks < 1) return hipSuccess;
   hipLaunchKernelGGL(gpass_tiles_kernel<kGpassTH>, dim3(n_vtiles, (4 / kGpassTH) * n_tblocks), dim3(256 * kGpassTH), 0,
                      st, (const bf16_t*)U, n_vtiles, (bf16_t*)G, ldG, (bf16_t*)Gt, ldGt, mtab, ldm, srow, Mrow, lse,
-                     rows, V);
+                     rows, V, nrows, row0);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -1537,12 +1784,12 @@ hipError_t launch_gfix(int in_bf16, int rows, int K, int V, const int* idx_s, co
 }
 
 hipError_t launch_splitk_sum(const float* part, int64_t pstride, int S, int64_t n, void* out, int out_bf16,
-                             hipStream_t st) {
-  if (n % 4 || pstride % 4) return hipErrorInvalidValue;
+                             const int* rowmap, const int* nrows, int row0, int d, hipStream_t st) {
+  if (n % 4 || pstride % 4 || (rowmap && (d % 4 || n % d))) return hipErrorInvalidValue;
   const int64_t n4 = n / 4;
   if (n4 <= 0) return hipSuccess;
   hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, pstride, S, n4,
-                     out, out_bf16);
+                     out, out_bf16, rowmap, nrows, row0, d);
   CKL_LAUNCH_CHECK();
   return hipSuccess;
 }

@@ -106,6 +106,22 @@ typedef struct {
                      /* (0 = V: W is the whole head).  idx holds ids in     */
                      /* [0, v_total); K <= v_total.  Only ckl_shard_forward,*/
                      /* ckl_shard_combine and ckl_backward accept a shard.  */
+  int64_t dw_group_rows; /* ckl_forward_backward only: rows of logit       */
+                     /* gradients kept for one fp32 update of dW, rounded  */
+                     /* down to whole chunks (at least one chunk).  0 =    */
+                     /* the default, min(16384, 8 * chunk rows).  Larger   */
+                     /* groups update dW less often (faster) and hold more */
+                     /* workspace (group rows x V x in_dtype).             */
+  int32_t compact_mask; /* 1: when a mask is given, the kept rows are      */
+                     /* gathered first (a packed copy of their H rows in   */
+                     /* the workspace) and every logit tile, recompute and */
+                     /* contraction runs over the kept rows only, so       */
+                     /* masked rows cost no matrix work; outputs are       */
+                     /* scattered back (masked rows: 0).  Teacher indices  */
+                     /* of masked rows are then not validated.  0: masked  */
+                     /* rows are computed and zeroed.  The workspace query */
+                     /* includes the packed copies when this is 1.         */
+  int32_t reserved_;  /* must be 0                                          */
 } ckl_problem;
 
 /* Workspace bytes needed by ckl_forward or ckl_shard_forward (which = 0),
@@ -178,11 +194,11 @@ ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
  * rounding of the non-teacher entries of G to in_dtype (u is rounded before
  * it is rescaled).
  *   ws: device workspace of at least ckl_workspace_size(p, 2) bytes: with
- *   n = the number of chunks, at most 16384 rows' worth and at least one,
- *   n + 1 chunk x V buffers of in_dtype (bf16: the forward's exponentials u
- *   of one chunk and G of n consecutive chunks; fp32: G of one chunk and G^T
- *   of n chunks; the fp32 update of dW runs once per n chunks), H^T and W^T,
- *   the dH split-k partials and small per-row arrays.
+ *   n = the number of chunks in one dW group (p->dw_group_rows, see
+ *   ckl_problem), n + 1 chunk x V buffers of in_dtype (bf16: the forward's
+ *   exponentials u of one chunk and G of n consecutive chunks; fp32: G of
+ *   one chunk and G^T of n chunks; the fp32 update of dW runs once per n
+ *   chunks), H^T and W^T, the dH split-k partials and small per-row arrays.
  * Rows per chunk: `chunk` rounded up to whole tiles (256 rows for bf16,
  * 128 for fp32), at most T rounded up. */
 ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void* W,
@@ -192,8 +208,19 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
 
 /* The chunk plan ckl_forward_backward uses for problem *p: out[0] = rows per
  * chunk, out[1] = number of chunks, out[2] = number of dH split-k parts,
- * out[3] = vocabulary columns per part.  Host-only; touches no device. */
-ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[4]);
+ * out[3] = vocabulary columns per part, out[4] = chunks per dW group.
+ * Host-only; touches no device. */
+ckl_status ckl_fused_plan(const ckl_problem* p, int64_t out[5]);
+
+/* Output finish for callers that keep fp32 gradients of the loss itself and
+ * learn the incoming gradient later (an autograd backward of the one-call
+ * path): dst[i] = scale * src[i] for i < n, rounded once to dst_dtype.
+ *   src:   [n] device float32;   dst: [n] device dst_dtype (may alias src
+ *          when dst_dtype is CKL_F32);
+ *   scale: [1] device float32 or NULL (= 1).
+ * src, dst 16-byte aligned, n a multiple of 4. */
+ckl_status ckl_scale_cast(const float* src, void* dst, int64_t n, int32_t dst_dtype, const float* scale,
+                          void* stream);
 
 /* Vocabulary-parallel shards (the README usage table's tensor-parallel
  * option shards the output head; the pages do not describe the exchange).

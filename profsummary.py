@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python -m chunked_kl_loss_amd.profsummary trace <kernel_stats.csv> <out.md> "<command>"
-    python -m chunked_kl_loss_amd.profsummary traffic <fetch_counter.csv> <write_counter.csv> \\
+    python profsummary.py trace <kernel_stats.csv> <out.md> "<command>"
+    python profsummary.py traffic <fetch_counter.csv> <write_counter.csv> \\
         <traffic.json> <workload> <path> <steps>
 
 `trace` condenses a --kernel-trace --stats run into a markdown table grouped by
@@ -65,7 +65,6 @@ def _per_dispatch(csv_path: str, counter: str):
 
 
 def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, path: str, steps: int) -> None:
-    sys.path.insert(0, ".")
     from bench import kernel_source_hash
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")

@@ -35,9 +35,16 @@ def to_device(x, device="cuda"):
     return H, W, idx, tl, mask
 
 
+def _host(t, as64):
+    return t.double().cpu().numpy() if as64 else t.float().cpu().numpy()
+
+
 def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False,
-            want_grads=True, teacher_form=0):
-    """Forward + backward through the C ABI.  Returns float64 numpy results."""
+            want_grads=True, teacher_form=0, compact=True, as64=True):
+    """Forward + backward through the C ABI.  Returns float64 numpy results
+    (float32 with as64=False: every GPU output is exactly representable).
+    compact: with a mask, the library packs the kept rows first (else masked
+    rows are computed and zeroed)."""
     import torch
 
     import chunked_kl_loss_amd as ckl
@@ -46,22 +53,22 @@ def run_gpu(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="in
         m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=np.uint8)).cuda()
     chunk = x.chunk if chunk is None else chunk
     loss, lse, row_loss = ckl.forward(H, W, idx, tl, m, chunk=chunk, validate=validate, want_row_loss=True,
-                                      teacher_form=teacher_form)
+                                      teacher_form=teacher_form, compact_mask=compact)
     out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy())
     if want_grads:
         g = torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
         dH, dW = ckl.backward(H, W, idx, tl, m, lse, g, chunk=chunk, dh_dtype=dh_dtype, dw_dtype=dw_dtype,
-                              validate=validate, teacher_form=teacher_form)
+                              validate=validate, teacher_form=teacher_form, compact_mask=compact)
         torch.cuda.synchronize()
-        out["dH"] = dH.double().cpu().numpy()
-        out["dW"] = dW.double().cpu().numpy()
+        out["dH"] = _host(dH, as64)
+        out["dW"] = _host(dW, as64)
     del H, W, idx, tl, m
     torch.cuda.empty_cache()
     return out
 
 
 def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, mask="inputs", validate=False,
-                  teacher_form=0):
+                  teacher_form=0, compact=True, dw_group_rows=0, as64=True):
     """The one-call forward + backward (no logit recompute) through the C ABI."""
     import torch
 
@@ -73,10 +80,11 @@ def run_gpu_fused(x, chunk=None, grad_loss=1.0, dh_dtype=None, dw_dtype=None, ma
     g = None if grad_loss is None else torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
     loss, lse, row_loss, dH, dW = ckl.forward_backward(H, W, idx, tl, m, g, chunk=chunk, dh_dtype=dh_dtype,
                                                        dw_dtype=dw_dtype, validate=validate, want_row_loss=True,
-                                                       teacher_form=teacher_form)
+                                                       teacher_form=teacher_form, compact_mask=compact,
+                                                       dw_group_rows=dw_group_rows)
     torch.cuda.synchronize()
     out = dict(loss=float(loss.item()), lse=lse.double().cpu().numpy(), row_loss=row_loss.double().cpu().numpy(),
-               dH=dH.double().cpu().numpy(), dW=dW.double().cpu().numpy())
+               dH=_host(dH, as64), dW=_host(dW, as64))
     del H, W, idx, tl, m, dH, dW
     torch.cuda.empty_cache()
     return out

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ckl_version() >> 16 == 1
+    assert lib.ckl_version() >> 16 == 2
 
 
 def test_status_strings(lib):
@@ -66,9 +66,14 @@ def _prob(**kw):
     (dict(K=3000, V=2048, v_total=2048), B.CKL_ERR_INVALID_ARG),
     (dict(teacher_form=-1), B.CKL_ERR_INVALID_ARG),
     (dict(V=4000001), B.CKL_ERR_UNSUPPORTED),
+    (dict(dw_group_rows=-1), B.CKL_ERR_INVALID_ARG),
+    (dict(compact_mask=2), B.CKL_ERR_INVALID_ARG),
 ])
 def test_problem_validation(lib, kw, status):
+    raw = {k: kw.pop(k) for k in ("compact_mask",) if k in kw}  # make_problem would coerce it to 0/1
     p = _prob(**kw)
+    for k, v in raw.items():
+        setattr(p, k, v)
     out = ctypes.c_size_t()
     assert lib.ckl_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == status
     assert lib.ckl_last_error()
@@ -174,6 +179,53 @@ def test_fused_plan_and_workspace(lib):
     # short sequences keep G of only the chunks they have
     one, two = ws(2048, 2048), ws(4096, 2048)
     assert two - one == pytest.approx(2048 * (201216 + 128) * 2, rel=0.05)
+    # the default dW group is at most eight chunks, so a smaller chunk holds less
+    assert ws(32768, 512) < ws(32768, 2048) < ws(32768, 2048) + 1
+    assert B.fused_plan(B.make_problem(32768, 2880, 201088, 100, 512))["dw_group_chunks"] == 8
+    assert B.fused_plan(B.make_problem(32768, 2880, 201088, 100, 2048))["dw_group_chunks"] == 8
+    assert B.fused_plan(B.make_problem(32768, 2880, 201088, 100, 8192))["dw_group_chunks"] == 2
+
+
+def test_fused_dw_group_budget(lib):
+    # dw_group_rows bounds the logit gradients kept per dW update: one chunk's
+    # worth keeps G of one chunk, saving the other seven chunks' rows
+    def prob(rows):
+        return B.make_problem(32768, 2880, 201088, 100, 2048, dw_group_rows=rows)
+    assert B.fused_plan(prob(2048))["dw_group_chunks"] == 1
+    assert B.fused_plan(prob(5000))["dw_group_chunks"] == 2       # rounded down to whole chunks
+    assert B.fused_plan(prob(1))["dw_group_chunks"] == 1          # at least one chunk
+    assert B.fused_plan(prob(1 << 20))["dw_group_chunks"] == 16   # at most every chunk
+    saved = B.workspace_size(prob(0), 2) - B.workspace_size(prob(2048), 2)
+    assert saved == pytest.approx(7 * 2048 * (201216 + 128) * 2, rel=1e-3)
+    # at one chunk per group the one-call path stays near the recomputing path's footprint
+    assert B.workspace_size(prob(2048), 2) < 1.6 * B.workspace_size(prob(0), 1)
+
+
+def test_packed_rows_workspace(lib):
+    # compact_mask adds the packed copy of H (T x d) and a few per-row arrays
+    for which in (0, 1, 2):
+        plain = B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048), which)
+        packed = B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048, compact_mask=True), which)
+        extra = packed - plain
+        if which == 1:  # the backward also accumulates dH in fp32 for the scatter (bf16 dH has it anyway)
+            assert extra == pytest.approx(32768 * 2880 * 2 + 16 * 32768, rel=0.01)
+        else:
+            assert extra == pytest.approx(32768 * 2880 * 2 + 16 * 32768, rel=0.01)
+    f32 = dict(dh_dtype=B.CKL_F32)
+    extra = (B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048, compact_mask=True, **f32), 1)
+             - B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048, **f32), 1))
+    assert extra == pytest.approx(32768 * 2880 * (2 + 4) + 16 * 32768, rel=0.01)
+
+
+def test_scale_cast_rejects_misuse(lib):
+    fake = 0x10000
+    assert lib.ckl_scale_cast(None, fake, 16, B.CKL_F32, None, None) == B.CKL_ERR_INVALID_ARG
+    assert lib.ckl_scale_cast(fake, fake + 0x1000, 6, B.CKL_F32, None, None) == B.CKL_ERR_INVALID_ARG  # n % 4
+    assert lib.ckl_scale_cast(fake, fake + 0x1000, 16, 5, None, None) == B.CKL_ERR_INVALID_ARG
+    assert lib.ckl_scale_cast(fake + 4, fake + 0x1000, 16, B.CKL_F32, None, None) == B.CKL_ERR_INVALID_ARG
+    assert lib.ckl_scale_cast(fake, fake + 0x1000, 16, B.CKL_F32, fake + 2, None) == B.CKL_ERR_INVALID_ARG
+    # a bf16 destination may not overlap the fp32 source
+    assert lib.ckl_scale_cast(fake, fake + 16, 16, B.CKL_BF16, None, None) == B.CKL_ERR_INVALID_ARG
 
 
 def test_shard_entry_points_reject_misuse(lib):
