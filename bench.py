@@ -3,20 +3,24 @@
 MI355X.
 
 One step = the loss and its gradients dH, dW over one batch of synthetic
-inputs that are resident in HBM before timing starts, either as
-ckl_forward + ckl_backward (--path recompute: the backward recomputes the
-logits chunk by chunk) or as one ckl_forward_backward call (--path fused: each
-row chunk's logits are multiplied once and kept).  Default workload:
-T = 32,768 rows, d = 2,880, V = 201,088, K = 100 cached teacher entries,
-chunk = 2,048, bf16 H and W (the pages' 32K-context, 201,088-token-vocabulary
-case).
+inputs that are resident in HBM before timing starts, either as one
+ckl_forward_backward call (--path fused: each row chunk's logits are
+multiplied once and kept) or as ckl_forward + ckl_backward (--path recompute:
+the backward recomputes the logits chunk by chunk, the pages' Full Chunked KL).
+Default workload: T = 32,768 rows, d = 2,880, V = 201,088, K = 100 cached
+teacher entries, chunk = 2,048, bf16 H and W (the pages' 32K-context,
+201,088-token-vocabulary case).
 
-Prints ONE JSON line with tokens/s, TFLOP/s (8 T V d useful flops per step),
-the fraction of the bf16 dense MFMA peak, peak HBM, a roofline entry for the
-dominant kernel (timed live with HIP events on the launch stream) and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: tokens/s, TFLOP/s (8 N V d useful flops per step over
+the N unmasked rows; also the flops the path actually multiplies), the
+fraction of the bf16 dense MFMA peak, peak HBM, a sampled-oracle parity check
+made before timing, a roofline entry for the dominant kernel (per-kernel HIP
+events on the launch stream, taken in a separate pass after the timed steps)
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload 2] [--path fused|recompute]
+    python bench.py --matrix     # workloads 1-4 and the packed-document chunk sweep,
+                                 # one child process per (workload, chunk); failures -> FAILED rows
 """
 from __future__ import annotations
 
@@ -25,6 +29,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -38,6 +43,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("chunked_kl_loss_amd/csrc/ckl_kernels.hip", "chunked_kl_loss_amd/csrc/ckl_tile.hpp",
                   "chunked_kl_loss_amd/csrc/ckl_common.hpp", "chunked_kl_loss_amd/csrc/ckl_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+METRIC = "fused KL fwd+bwd tokens/s and TFLOP/s (% MFMA bf16 peak); peak HBM GiB"
 
 
 def kernel_source_hash() -> str:
@@ -50,6 +56,17 @@ def kernel_source_hash() -> str:
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def upload(x, dev):
@@ -86,9 +103,305 @@ def cpu_baseline(x, rows: int):
     dt = time.perf_counter() - t0
     assert np.isfinite(r["loss"])
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"first {rows} of {x.T} rows of the same workload (full d={x.d}, V={x.V}, K={x.K}); "
                       f"fp64 dense forward + backward in {dt:.1f} s",
             "seconds": dt}
+
+
+def parity_sample(x, got, n_rows: int = 6, n_vrows: int = 4, seed: int = 5):
+    """Sampled-oracle parity of one step's outputs: rows of LSE, per-row KL
+    and dH computed one by one by the fp64 oracle, rows of dW from the
+    oracle given the GPU's LSE (checked first on the sampled rows), and the
+    loss against the masked mean of the GPU's row losses.  Tolerances are the
+    parity tests' (bf16: loss 2e-3 relative, gradients 1e-2 of the largest
+    reference entry; fp32: 1e-5)."""
+    import numpy as np
+
+    import oracle
+    tol = dict(loss=2e-3, grad=1e-2, lse=2e-3) if x.dtype == "bf16" else dict(loss=1e-5, grad=1e-5, lse=1e-5)
+    rng = np.random.default_rng(seed)
+    keep = np.ones(x.T, bool) if x.mask is None else x.mask != 0
+    kept = np.nonzero(keep)[0]
+    rows = np.unique(np.concatenate([[kept[0], kept[-1]], rng.choice(kept, size=max(0, n_rows - 2))]))
+    t0 = time.perf_counter()
+    ref = oracle.kl_rows(x.H, x.W, x.idx, x.tlogit, rows, mask=x.mask)
+    e_lse = float(np.abs(got["lse"][rows] - ref["lse"]).max())
+    e_rl = float((np.abs(got["row_loss"][rows] - ref["row_loss"]) / np.abs(ref["row_loss"])).max())
+    e_dh = float(np.abs(got["dH"][rows] - ref["dH"]).max() / np.abs(ref["dH"]).max())
+    vrows = np.unique(np.concatenate([[0, x.V - 1], rng.integers(0, x.V, size=max(0, n_vrows - 2))]))
+    dw_ref = oracle.dw_rows(x.H, x.W, x.idx, x.tlogit, vrows, got["lse"].astype(np.float64), mask=x.mask)
+    e_dw = float(np.abs(got["dW"][vrows] - dw_ref).max() / np.abs(dw_ref).max())
+    mean_rows = float(got["row_loss"][keep].astype(np.float64).sum() / keep.sum())
+    e_loss = abs(got["loss"] - mean_rows) / abs(mean_rows)
+    ok = (e_lse <= tol["lse"] and e_rl <= tol["loss"] and e_dh <= tol["grad"] and e_dw <= tol["grad"]
+          and e_loss <= 1e-5 and bool((got["dH"][~keep] == 0).all()))
+    return {"pass": bool(ok), "rows": [int(r) for r in rows], "vocab_rows": [int(v) for v in vrows],
+            "lse_abs_err": e_lse, "row_loss_rel_err": e_rl, "dH_rel_err": e_dh, "dW_rel_err": e_dw,
+            "loss_vs_row_mean_rel": e_loss, "oracle_s": time.perf_counter() - t0}
+
+
+def run(args) -> dict:
+    """One workload, one path, in this process.  Returns the result row."""
+    import numpy as np
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    from chunked_kl_loss_amd import _binding as B
+    from synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    lib = ckl.load_library()
+    w = WORKLOADS[args.workload]
+    chunk = args.chunk or w.chunk
+    log(f"generating workload {w.name} (seed {args.seed}) ...")
+    t0 = time.perf_counter()
+    x = make_inputs(w, seed=args.seed)
+    log(f"  inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.empty(1, device=dev)  # initialise the context before resetting the peak counter
+    torch.cuda.reset_peak_memory_stats(dev)
+    H, W, idx, tl, mask = upload(x, dev)
+    T, d, V, K = x.T, x.d, x.V, x.K
+    n_kept = int(T if x.mask is None else x.mask.sum())
+    packed = mask is not None and not args.no_compact
+    in_code = B.CKL_BF16 if x.dtype == "bf16" else B.CKL_F32
+    prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32, compact_mask=packed,
+                          dw_group_rows=args.dw_group_rows)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = ctypes.byref(prob)
+    mp = None if mask is None else mask.data_ptr()
+    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    rows_mult = n_kept if packed else T  # rows whose logits the path multiplies
+
+    def measure(path: str, steps: int, warmup: int, check: bool) -> dict:
+        fused = path == "fused"
+        plan = B.fused_plan(prob) if fused else B.backward_plan(prob)
+        torch.cuda.reset_peak_memory_stats(dev)
+        ws_f = torch.empty(B.workspace_size(prob, 2 if fused else 0), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(1 if fused else B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+        row_loss = torch.empty(T, dtype=torch.float32, device=dev)
+        dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+        rl = row_loss.data_ptr() if check else None
+
+        def fwd():
+            B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                    loss.data_ptr(), lse.data_ptr(), rl, ws_f.data_ptr(), ws_f.numel(), sp), lib)
+
+        def bwd():
+            B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                     lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(),
+                                     ws_b.numel(), sp), lib)
+
+        def both():
+            B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
+                                             None, loss.data_ptr(), lse.data_ptr(), rl, dH.data_ptr(),
+                                             dW.data_ptr(), ws_f.data_ptr(), ws_f.numel(), sp), lib)
+
+        if fused:
+            fwd, bwd = both, (lambda: None)
+        log(f"warmup {warmup} steps; path {path}, plan {plan}")
+        for _ in range(max(warmup, 1 if check else 0)):
+            fwd()
+            bwd()
+        torch.cuda.synchronize(dev)
+        if not np.isfinite(loss.item()):
+            raise RuntimeError("non-finite loss")
+        parity = None
+        if check:
+            got = dict(loss=float(loss.item()), lse=lse.cpu().numpy(), row_loss=row_loss.cpu().numpy(),
+                       dH=dH.float().cpu().numpy(), dW=dW.cpu().numpy())
+            parity = parity_sample(x, got)
+            log(f"parity (sampled oracle rows): {parity}")
+            del got
+            rl = None  # the timed steps do not write the row losses
+            torch.cuda.synchronize(dev)
+            # the parity check's host copies are not part of a step's footprint
+            torch.cuda.reset_peak_memory_stats(dev)
+            fwd()
+            bwd()
+            torch.cuda.synchronize(dev)
+        # timed steps: no per-kernel events
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize(dev)
+        t_start = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fwd()
+            ev[i][1].record(stream)
+            bwd()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t_start
+        fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+        bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+        step_ms = wall * 1e3 / steps
+        peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+        log(f"timed {steps} steps, path {path}: {step_ms:.2f} ms/step")
+        # per-kernel pass: the same steps again with the library's events on
+        kt = None
+        if args.kernel_steps > 0:
+            ckl.timing_enable(True)
+            for _ in range(args.kernel_steps):
+                fwd()
+                bwd()
+            torch.cuda.synchronize(dev)
+            kt = ckl.timing_read()
+            ckl.timing_enable(False)
+        del ws_f, ws_b, dH, dW, loss, lse, row_loss
+        torch.cuda.empty_cache()
+        return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, kt=kt, parity=parity,
+                    fwd_ms=None if fused else float(np.mean(fwd_ms)),
+                    bwd_ms=None if fused else float(np.mean(bwd_ms)),
+                    events_min_ms=float(np.min(np.add(fwd_ms, bwd_ms))))
+
+    m = measure(args.path, args.steps, args.warmup, check=args.parity)
+    fused = args.path == "fused"
+    step_ms, kt, plan = m["step_ms"], m["kt"], m["plan"]
+
+    flops_useful = 8.0 * n_kept * V * d
+    flops_mult = (6.0 if fused else 8.0) * rows_mult * V * d
+    roofline = None
+    kernels = None
+    if kt is not None:
+        ks = args.kernel_steps
+        algo_flops = {"fwd_lse": 2.0 * rows_mult * V * d, "gemm_dhdw": 4.0 * rows_mult * V * d}
+        if not fused:
+            algo_flops["bwd_grad"] = 2.0 * rows_mult * V * d
+        kernels = {k: {"total_ms_per_step": ms / ks, "launches_per_step": n / ks,
+                       "avg_launch_ms": (ms / n if n else 0.0)} for k, (ms, n) in kt.items()}
+        dom = max(algo_flops, key=lambda k: kt[k][0])
+        dom_ms, dom_n = kt[dom]
+        achieved = algo_flops[dom] * ks / (dom_ms * 1e-3) / 1e12
+        traffic = None
+        try:
+            with open(TRAFFIC_FILE) as fh:
+                tr = json.load(fh)
+            for e in tr.get("entries", []):
+                ent = e.get("kernels", {}).get(dom)
+                if (ent and e.get("source_hash") == kernel_source_hash() and e.get("workload") == w.name
+                        and e.get("path") == args.path and chunk == w.chunk):
+                    traffic = ent["hbm_bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            pass
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": traffic,
+                    "avg_launch_ms": dom_ms / dom_n, "launches_per_step": dom_n / ks,
+                    "algorithmic_flops_per_step": algo_flops[dom],
+                    "algorithmic_flops_per_launch": algo_flops[dom] / (dom_n / ks),
+                    "timing": f"HIP events around each launch on the launch stream, {ks} steps after the timed ones"}
+    result = {
+        "metric": METRIC,
+        "value": T / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generator: H~N(0,1), W~N(0,1/d), K distinct uniform teacher indices, "
+                "teacher logits N(0,2) sorted" + ("; packed documents, first quarter of each masked)"
+                                                  if x.mask is not None else ")"),
+        "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "chunk": chunk,
+                   "masked_rows": T - n_kept, "packed_rows": packed, "parallelism": "single GPU",
+                   "path": args.path, "plan": plan},
+        "kept_tokens_per_s": n_kept / (step_ms * 1e-3),
+        "tflops": flops_useful / (step_ms * 1e-3) / 1e12,
+        "tflops_note": "8 N V d flops per step over the N unmasked rows, the method's count (forward, "
+                       "recomputed logits, dH, dW); tflops_multiplied counts what the path multiplies: "
+                       + ("6 x rows V d (no recompute)" if fused else "8 x rows V d")
+                       + (", rows = kept rows (masked rows packed away)" if packed else ", rows = T"),
+        "tflops_multiplied": flops_mult / (step_ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * flops_mult / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "peak_hbm_gib": m["peak_gib"],
+        "fwd_ms": m["fwd_ms"],
+        "bwd_ms": m["bwd_ms"],
+        "step_ms_events_min": m["events_min_ms"],
+        "parity": m["parity"],
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if args.compare:
+        other = "recompute" if fused else "fused"
+        o = measure(other, args.steps, args.warmup, check=False)
+        result["other_path"] = {"path": other, "ms_per_step": o["step_ms"], "tokens_per_s": T / (o["step_ms"] * 1e-3),
+                                "peak_hbm_gib": o["peak_gib"], "fwd_ms": o["fwd_ms"], "bwd_ms": o["bwd_ms"],
+                                "tflops_multiplied": (6.0 if other == "fused" else 8.0) * rows_mult * V * d
+                                / (o["step_ms"] * 1e-3) / 1e12,
+                                "plan": o["plan"],
+                                "kernels_ms_per_step": ({k: ms / args.kernel_steps for k, (ms, n) in o["kt"].items()
+                                                         if n} if o["kt"] else None)}
+        result["other_path"]["pct_bf16_peak"] = 100.0 * result["other_path"]["tflops_multiplied"] / PEAK_BF16_TFLOPS
+    del H, W, idx, tl, mask
+    torch.cuda.empty_cache()
+    if args.copy_calibration:
+        # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        result["copy_calibration_bytes"] = 1 << 30
+        del src, dst
+    if args.cpu_rows > 0:
+        log(f"oracle CPU baseline on {args.cpu_rows} rows ...")
+        result["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, x.T))
+    return result
+
+
+def matrix(args) -> dict:
+    """Workloads 1-4 and the packed-document chunk sweep, each (workload,
+    chunk, path) in its own child process (started before this process
+    touches the GPU); a child that fails or runs out of memory gives a FAILED
+    row and the sweep goes on."""
+    from synth import WORKLOADS
+    cases = [(1, None), (2, None), (3, None)] + [(4, c) for c in WORKLOADS[4].chunk_sweep]
+    rows = []
+    for wl, chunk in cases:
+        for path in ("fused", "recompute"):
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", str(wl), "--path", path,
+                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-compare",
+                   "--cpu-rows", "0", "--kernel-steps", "0"]
+            if chunk:
+                cmd += ["--chunk", str(chunk)]
+            name = f"workload {wl} chunk {chunk or WORKLOADS[wl].chunk} path {path}"
+            log(f"matrix: {name}")
+            t0 = time.perf_counter()
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=args.case_timeout)
+                line = r.stdout.strip().splitlines()[-1] if r.returncode == 0 and r.stdout.strip() else ""
+                row = json.loads(line) if line else None
+                err = None if row else (r.stderr.strip().splitlines() or ["no output"])[-1]
+            except subprocess.TimeoutExpired:
+                row, err = None, f"timed out after {args.case_timeout} s"
+            if row is None:
+                rows.append({"workload": WORKLOADS[wl].name, "chunk": chunk or WORKLOADS[wl].chunk, "path": path,
+                             "status": "FAILED", "error": err})
+                log(f"  FAILED: {err}")
+                continue
+            c = row["config"]
+            rows.append({"workload": c["workload"], "chunk": c["chunk"], "path": path, "status": "ok",
+                         "T": c["T"], "kept_rows": c["T"] - c["masked_rows"], "packed_rows": c["packed_rows"],
+                         "ms_per_step": row["ms_per_step"], "tokens_per_s": row["value"],
+                         "tflops_useful": row["tflops"], "tflops_multiplied": row["tflops_multiplied"],
+                         "pct_bf16_peak": row["pct_bf16_peak"], "peak_hbm_gib": row["peak_hbm_gib"],
+                         "parity": row["parity"], "wall_s": time.perf_counter() - t0})
+            log(f"  {row['ms_per_step']:.1f} ms/step, peak {row['peak_hbm_gib']:.2f} GiB, "
+                f"parity {'pass' if row['parity'] and row['parity']['pass'] else 'FAIL'}")
+    return {"metric": METRIC, "matrix": rows, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "isolation": "one child process per (workload, chunk, path)"}
 
 
 def main():
@@ -104,194 +417,23 @@ def main():
                     help="one ckl_forward_backward call per step, or ckl_forward + ckl_backward")
     ap.add_argument("--compare", action=argparse.BooleanOptionalAction, default=True,
                     help="after the timed path, also time the other one (reported under other_path)")
+    ap.add_argument("--parity", action=argparse.BooleanOptionalAction, default=True,
+                    help="check sampled rows against the fp64 oracle before timing")
+    ap.add_argument("--kernel-steps", type=int, default=3,
+                    help="steps of the separate per-kernel timing pass (0 = skip; no roofline entry)")
+    ap.add_argument("--no-compact", action="store_true", help="masked workloads: compute masked rows too")
+    ap.add_argument("--dw-group-rows", type=int, default=0, help="one-call path: rows per dW update (0 = default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
+    ap.add_argument("--matrix", action="store_true", help="the workload matrix, one child process per case")
+    ap.add_argument("--case-timeout", type=int, default=300, help="--matrix: seconds per case")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the loss shards by rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import chunked_kl_loss_amd as ckl
-    from chunked_kl_loss_amd import _binding as B
-    from synth import WORKLOADS, make_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    lib = ckl.load_library()
-    w = WORKLOADS[args.workload]
-    chunk = args.chunk or w.chunk
-    log(f"generating workload {w.name} (seed {args.seed}) ...")
-    t0 = time.perf_counter()
-    x = make_inputs(w, seed=args.seed)
-    log(f"  inputs ready in {time.perf_counter() - t0:.1f} s")
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    torch.empty(1, device=dev)  # initialise the context before resetting the peak counter
-    torch.cuda.reset_peak_memory_stats(dev)
-    H, W, idx, tl, mask = upload(x, dev)
-    T, d, V, K = x.T, x.d, x.V, x.K
-    in_code = B.CKL_BF16 if x.dtype == "bf16" else B.CKL_F32
-    prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    P = ctypes.byref(prob)
-    mp = None if mask is None else mask.data_ptr()
-    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
-
-    def measure(path: str, steps: int, warmup: int) -> dict:
-        """Time `steps` steps of one path (inputs already resident); per-kernel event timing included."""
-        fused = path == "fused"
-        plan = B.fused_plan(prob) if fused else B.backward_plan(prob)
-        torch.cuda.reset_peak_memory_stats(dev)
-        ws_f = torch.empty(B.workspace_size(prob, 2 if fused else 0), dtype=torch.uint8, device=dev)
-        ws_b = torch.empty(1 if fused else B.workspace_size(prob, 1), dtype=torch.uint8, device=dev)
-        loss = torch.empty(1, dtype=torch.float32, device=dev)
-        lse = torch.empty(T, dtype=torch.float32, device=dev)
-        dH = torch.empty((T, d), dtype=H.dtype, device=dev)
-        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
-
-        def fwd():
-            B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
-                                    loss.data_ptr(), lse.data_ptr(), None, ws_f.data_ptr(), ws_f.numel(), sp), lib)
-
-        def bwd():
-            B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
-                                     lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(),
-                                     ws_b.numel(), sp), lib)
-
-        def both():
-            B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
-                                             None, loss.data_ptr(), lse.data_ptr(), None, dH.data_ptr(),
-                                             dW.data_ptr(), ws_f.data_ptr(), ws_f.numel(), sp), lib)
-
-        if fused:
-            fwd, bwd = both, (lambda: None)
-        log(f"warmup {warmup} steps; path {path}, plan {plan}")
-        for _ in range(warmup):
-            fwd()
-            bwd()
-        torch.cuda.synchronize(dev)
-        if not np.isfinite(loss.item()):
-            raise RuntimeError("non-finite loss")
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        ckl.timing_enable(True)
-        torch.cuda.synchronize(dev)
-        t_start = time.perf_counter()
-        for i in range(steps):
-            ev[i][0].record(stream)
-            fwd()
-            ev[i][1].record(stream)
-            bwd()
-            ev[i][2].record(stream)
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - t_start
-        ckl.timing_enable(False)
-        fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
-        bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
-        step_ms = wall * 1e3 / steps
-        peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
-        log(f"timed {steps} steps, path {path}: {step_ms:.2f} ms/step")
-        kt = ckl.timing_read()
-        del ws_f, ws_b, dH, dW, loss, lse
-        torch.cuda.empty_cache()
-        return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, kt=kt,
-                    fwd_ms=None if fused else float(np.mean(fwd_ms)),
-                    bwd_ms=None if fused else float(np.mean(bwd_ms)),
-                    events_min_ms=float(np.min(np.add(fwd_ms, bwd_ms))))
-
-    m = measure(args.path, args.steps, args.warmup)
-    fused = args.path == "fused"
-    step_ms, kt, plan = m["step_ms"], m["kt"], m["plan"]
-
-    # ---- per-kernel timing and roofline of the dominant kernel
-    flops_step = 8.0 * T * V * d
-    performed_step = (6.0 if fused else 8.0) * T * V * d
-    algo_flops = {"fwd_lse": 2.0 * T * V * d, "gemm_dhdw": 4.0 * T * V * d}
-    if not fused:
-        algo_flops["bwd_grad"] = 2.0 * T * V * d
-    kernels = {k: {"total_ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
-                   "avg_launch_ms": (ms / n if n else 0.0)} for k, (ms, n) in kt.items()}
-    dom = max(algo_flops, key=lambda k: kt[k][0])
-    dom_ms, dom_n = kt[dom]
-    achieved = algo_flops[dom] * args.steps / (dom_ms * 1e-3) / 1e12
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
-        for e in tr.get("entries", []):
-            ent = e.get("kernels", {}).get(dom)
-            if (ent and e.get("source_hash") == kernel_source_hash() and e.get("workload") == w.name
-                    and e.get("path") == args.path and chunk == w.chunk):
-                traffic = ent["hbm_bytes_per_launch"]
-    except (OSError, ValueError, KeyError):
-        pass
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": traffic,
-                "avg_launch_ms": dom_ms / dom_n, "launches_per_step": dom_n / args.steps,
-                "algorithmic_flops_per_step": algo_flops[dom],
-                "algorithmic_flops_per_launch": algo_flops[dom] / (dom_n / args.steps)}
-    tokens_s = T / (step_ms * 1e-3)
-    tflops = flops_step / (step_ms * 1e-3) / 1e12
-    n_valid = int(T if x.mask is None else x.mask.sum())
-    result = {
-        "metric": "fused KL fwd+bwd tokens/s and TFLOP/s (% MFMA bf16 peak); peak HBM GiB",
-        "value": tokens_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": step_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if x.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded generator: H~N(0,1), W~N(0,1/d), K distinct uniform teacher indices, "
-                "teacher logits N(0,2) sorted)",
-        "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "chunk": chunk,
-                   "masked_rows": T - n_valid, "parallelism": "single GPU", "path": args.path,
-                   "plan": plan},
-        "tflops": tflops,
-        "tflops_note": "8 T V d flops per step, the method's count (forward, recomputed logits, dH, dW)"
-                       + ("; the fused path multiplies 6 T V d of them (no recompute)" if fused else ""),
-        "tflops_multiplied": performed_step / (step_ms * 1e-3) / 1e12,
-        "pct_bf16_peak": 100.0 * performed_step / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "peak_hbm_gib": m["peak_gib"],
-        "fwd_ms": m["fwd_ms"],
-        "bwd_ms": m["bwd_ms"],
-        "step_ms_events_min": m["events_min_ms"],
-        "kernels": kernels,
-        "roofline": roofline,
-        "cpu_baseline": None,
-    }
-    if args.compare:
-        other = "recompute" if fused else "fused"
-        o = measure(other, args.steps, args.warmup)
-        result["other_path"] = {"path": other, "ms_per_step": o["step_ms"], "tokens_per_s": T / (o["step_ms"] * 1e-3),
-                                "peak_hbm_gib": o["peak_gib"], "fwd_ms": o["fwd_ms"], "bwd_ms": o["bwd_ms"],
-                                "plan": o["plan"],
-                                "kernels_ms_per_step": {k: ms / args.steps for k, (ms, n) in o["kt"].items() if n}}
-    del H, W, idx, tl, mask
-    torch.cuda.empty_cache()
-    if args.copy_calibration:
-        # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize(dev)
-        dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        result["copy_calibration_bytes"] = 1 << 30
-        del src, dst
-    if args.cpu_rows > 0:
-        log(f"oracle CPU baseline on {args.cpu_rows} rows ...")
-        result["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, x.T))
+    result = matrix(args) if args.matrix else run(args)
     print(json.dumps(result), flush=True)
 
 
