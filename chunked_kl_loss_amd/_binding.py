@@ -26,6 +26,7 @@ CKL_TEACHER_LOGPROBS = 1
 EXPORTED = (
     "ckl_workspace_size",
     "ckl_forward",
+    "ckl_forward_noalloc",
     "ckl_backward",
     "ckl_backward_plan",
     "ckl_forward_backward",
@@ -86,6 +87,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckl_workspace_size.restype = i32
     lib.ckl_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ckl_forward.restype = i32
+    lib.ckl_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ckl_forward_noalloc.restype = i32
     lib.ckl_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ckl_backward.restype = i32
     lib.ckl_backward_plan.argtypes = [P, i64p]

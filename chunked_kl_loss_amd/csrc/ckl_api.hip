@@ -87,9 +87,13 @@ struct TimingState {
 TimingState g_timing;
 
 // Launch `fn` (returning hipError_t), bracketed by timing events when enabled.
+// Set while ckl_forward_noalloc runs: its launches record no timing events
+// (creating events would allocate).
+thread_local bool g_no_events = false;
+
 template <class Fn>
 hipError_t timed(int cls, hipStream_t st, Fn&& fn) {
-  if (!g_timing.on) return fn();
+  if (!g_timing.on || g_no_events) return fn();
   std::pair<hipEvent_t, hipEvent_t> ev{};
   {
     std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -428,6 +432,34 @@ hipError_t pack_rows(const Plan& q, const Packed& k, const uint8_t* mask, const 
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// ------------------------------------------------ allocation-free forward --
+// ckl_forward_noalloc takes its workspace from this file-scope device array
+// instead of a caller's buffer.  Every device the library runs on holds its
+// own copy until the process ends; host code must never pass the array's
+// name to a kernel (in host code it is only a stand-in): it uses the device
+// address looked up once per device, with that device current, on the entry
+// point's first call there.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+ckl_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CKL_ERR_UNSUPPORTED, "device ordinal %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "looking up the device scratch array");
+    if (ptr == nullptr) return fail(CKL_ERR_HIP, "the device scratch array has no address");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return CKL_OK;
+}
+
 ckl_status check_validate_flag(int* bad_dev, hipStream_t st) {
   int h = 0;
   HIP_TRY(hipMemcpyAsync(&h, bad_dev, sizeof(int), hipMemcpyDeviceToHost, st), "reading index check flag");
@@ -543,6 +575,38 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
               "scatter row loss");
   }
   return CKL_OK;
+}
+
+ckl_status ckl_forward_noalloc(const ckl_problem* p, const void* H, const void* W, const int32_t* idx,
+                               const float* tlogit, const uint8_t* mask, float* loss, float* lse, float* row_loss,
+                               void* stream) {
+  ckl_status s = check_problem(p);
+  if (s != CKL_OK) return s;
+  if (p->validate)
+    return fail(CKL_ERR_UNSUPPORTED, "ckl_forward_noalloc does not validate indices (that reads a flag back "
+                                     "and synchronises): use ckl_forward");
+  const Plan q = make_plan(p);
+  const size_t need = fwd_layout(q, p).total;
+  if (need > kScratchBytes)
+    return fail(CKL_ERR_UNSUPPORTED,
+                "forward workspace of %zu bytes exceeds the %zu-byte device scratch array of ckl_forward_noalloc "
+                "(use ckl_forward with a workspace)",
+                need, kScratchBytes);
+  hipStream_t st = (hipStream_t)stream;
+  if (st != nullptr) {
+    int cur = -1, sdev = -1;
+    HIP_TRY(hipGetDevice(&cur), "hipGetDevice");
+    HIP_TRY(hipStreamGetDevice(st, &sdev), "hipStreamGetDevice");
+    if (cur != sdev)
+      return fail(CKL_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", sdev, cur);
+  }
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws);
+  if (s != CKL_OK) return s;
+  g_no_events = true;
+  s = ckl_forward(p, H, W, idx, tlogit, mask, loss, lse, row_loss, ws, kScratchBytes, stream);
+  g_no_events = false;
+  return s;
 }
 
 ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, const int32_t* idx, const float* tlogit,

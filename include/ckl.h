@@ -147,6 +147,26 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W,
                        float* loss, float* lse, float* row_loss,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ckl_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The workspace is a file-scope device array of the
+ * library, 64 MiB per device, held by every device the library runs on until
+ * the process ends; the call allocates nothing (no hipMalloc, no events).
+ * Arguments and results as in ckl_forward.  Limits and errors:
+ *   - the problem's forward workspace, ckl_workspace_size(p, 0), must fit in
+ *     64 MiB (about 50,000 rows at K = 100 without packed rows), else
+ *     CKL_ERR_UNSUPPORTED and nothing is launched;
+ *   - validate = 1 is refused (CKL_ERR_UNSUPPORTED): the index check reads a
+ *     flag back and synchronises;
+ *   - `stream` must belong to the current device (CKL_ERR_INVALID_ARG).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one device race and give undefined results; calls on one stream, or
+ * ordered between streams, do not overlap. */
+ckl_status ckl_forward_noalloc(const ckl_problem* p, const void* H, const void* W,
+                               const int32_t* idx, const float* tlogit, const uint8_t* mask,
+                               float* loss, float* lse, float* row_loss, void* stream);
+
 /* Backward pass: dH and dW of grad_loss * loss.
  *   lse:       [T] from ckl_forward on the same inputs (or from
  *              ckl_shard_combine; on a vocabulary shard dW is the shard's

@@ -249,3 +249,18 @@ def test_shard_entry_points_reject_misuse(lib):
     st = lib.ckl_shard_combine(ctypes.byref(shard), 0, fake, fake, fake, fake, None, fake, fake, None, fake, 1 << 30,
                                None)
     assert st == B.CKL_ERR_INVALID_ARG
+
+
+def test_noalloc_forward_refusals(lib):
+    # refused on the host before any device work: a workspace beyond the
+    # 64 MiB device scratch array, and index validation (it synchronises)
+    fake = 0x10000
+    too_big = B.make_problem(200000, 2880, 201088, 100, 2048)
+    assert B.workspace_size(too_big, 0) > 64 << 20
+    st = lib.ckl_forward_noalloc(ctypes.byref(too_big), fake, fake, fake, fake, None, fake, fake, None, None)
+    assert st == B.CKL_ERR_UNSUPPORTED
+    val = B.make_problem(100, 64, 1000, 8, 64, validate=True)
+    st = lib.ckl_forward_noalloc(ctypes.byref(val), fake, fake, fake, fake, None, fake, fake, None, None)
+    assert st == B.CKL_ERR_UNSUPPORTED
+    # the headline forward fits
+    assert B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048), 0) <= 64 << 20
