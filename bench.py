@@ -109,6 +109,100 @@ def cpu_baseline(x, rows: int):
             "seconds": dt}
 
 
+# A microbenchmark of the dense bf16 MFMA rate the chip sustains: every wave
+# of 8-wave workgroups issues v_mfma_f32_32x32x16_bf16 back to back from
+# registers (no memory traffic), its operands either N(0,1)-like bf16 values
+# that change from one instruction to the next (what a contraction of random
+# data sees) or one constant.  The board's power limit lowers the clock with
+# the operands' switching activity, so the first figure is the practical
+# ceiling for this path's data and the published 2.5 PFLOP/s the second's
+# limit.
+MFMA_PEAK_SRC = r"""
+#include <hip/hip_runtime.h>
+#include <cstdio>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ unsigned mix(unsigned x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16; return x;
+}
+__device__ __forceinline__ __bf16 val(unsigned h) {
+  return (__bf16)(1.7f * ((h & 0xffff) / 65536.f + (h >> 16) / 65536.f - 1.f));
+}
+template <int RAND>
+__global__ __launch_bounds__(512) void mfma_peak(int iters, float* out) {
+  bf16x8 a[8], b[4];
+  const unsigned s = blockIdx.x * 512 + threadIdx.x;
+  for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < 8; ++e) a[i][e] = RAND ? val(mix(s * 131u + i * 8 + e)) : (__bf16)0.5f;
+  for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 8; ++e) b[i][e] = RAND ? val(mix(s * 977u + 4099u + i * 8 + e)) : (__bf16)0.25f;
+  f32x16 c[8] = {};
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[(i * 4 + j) & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[(i * 4 + j) & 7], 0, 0, 0);
+  float t = 0.f;
+  for (int j = 0; j < 8; ++j)
+    for (int r = 0; r < 16; ++r) t += c[j][r];
+  out[blockIdx.x * 512 + threadIdx.x] = t;
+}
+int main() {
+  const int iters = 2000, blocks = 1024;
+  float* out;
+  if (hipMalloc(&out, (size_t)blocks * 512 * 4) != hipSuccess) return 1;
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
+  for (int rnd = 1; rnd >= 0; --rnd) {
+    float best = 1e30f;
+    for (int rep = 0; rep < 3; ++rep) {
+      (void)hipEventRecord(e0);
+      if (rnd) hipLaunchKernelGGL(mfma_peak<1>, dim3(blocks), dim3(512), 0, 0, iters, out);
+      else hipLaunchKernelGGL(mfma_peak<0>, dim3(blocks), dim3(512), 0, 0, iters, out);
+      (void)hipEventRecord(e1);
+      (void)hipEventSynchronize(e1);
+      float ms;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (ms < best) best = ms;
+    }
+    printf("%s %.3f\n", rnd ? "random" : "constant", (double)blocks * 8 * 32 * 32768.0 * iters / best / 1e9);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+"""
+
+
+def mfma_peak():
+    """Measured bf16 MFMA rate (TFLOP/s) with random and constant operands, from
+    the microbenchmark above built with hipcc for gfx950 and run as a child
+    process; None if it cannot be built or run."""
+    import shutil
+    import tempfile
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc):
+        hipcc = shutil.which("hipcc")
+    if not hipcc:
+        return None
+    with tempfile.TemporaryDirectory() as tmp:
+        src, exe = os.path.join(tmp, "mfma_peak.hip"), os.path.join(tmp, "mfma_peak")
+        with open(src, "w") as f:
+            f.write(MFMA_PEAK_SRC)
+        r = subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature", "-Xclang",
+                            "-packed-fp32-ops", src, "-o", exe], capture_output=True, text=True)
+        if r.returncode != 0:
+            log(f"mfma peak probe did not build: {r.stderr[-300:]}")
+            return None
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        if r.returncode != 0:
+            return None
+        vals = dict(line.split() for line in r.stdout.strip().splitlines())
+        return {"random_operands_tflops": float(vals["random"]), "constant_operands_tflops": float(vals["constant"]),
+                "unit": "TFLOP/s",
+                "note": "v_mfma_f32_32x32x16_bf16 back to back from registers, 8 waves per CU, no memory traffic"}
+
+
 def parity_sample(x, got, n_rows: int = 6, n_vrows: int = 4, seed: int = 5):
     """Sampled-oracle parity of one step's outputs: rows of LSE, per-row KL
     and dH computed one by one by the fp64 oracle, rows of dW from the
@@ -426,6 +520,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
     ap.add_argument("--matrix", action="store_true", help="the workload matrix, one child process per case")
+    ap.add_argument("--mfma-peak", action=argparse.BooleanOptionalAction, default=True,
+                    help="measure the sustained bf16 MFMA rate with a microbenchmark (hipcc, child process)")
     ap.add_argument("--case-timeout", type=int, default=300, help="--matrix: seconds per case")
     args = ap.parse_args()
 
@@ -433,7 +529,13 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the loss shards by rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    peak = mfma_peak() if args.mfma_peak and not args.matrix else None  # before this process touches the GPU
     result = matrix(args) if args.matrix else run(args)
+    if peak is not None:
+        result["measured_mfma_peak"] = peak
+        if result.get("roofline"):
+            result["roofline"]["frac_of_measured_random_peak"] = (
+                result["roofline"]["achieved"] / peak["random_operands_tflops"])
     print(json.dumps(result), flush=True)
 
 

@@ -5,7 +5,12 @@
         <traffic.json> <workload> <path> <steps>
 
 `trace` condenses a --kernel-trace --stats run into a markdown table grouped by
-kernel class.  `traffic` takes the FETCH_SIZE and WRITE_SIZE passes (KiB per
+kernel class.  `counters` condenses --pmc runs (with --kernel-trace) into a
+per-class table of clock, MFMA-busy fraction, achieved MFMA rate and LDS
+figures:
+
+    python profsummary.py counters <out.md> "<title>" <counter_collection.csv> ["<command>"] ...
+  `traffic` takes the FETCH_SIZE and WRITE_SIZE passes (KiB per
 dispatch), scales them by what the same counters read for the plain 1 GiB
 copy that bench.py --copy-calibration runs, and records HBM bytes per launch
 for every kernel class in traffic.json under (workload, path), tagged with the
@@ -97,9 +102,66 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, workload: str, path: 
     json.dump({"entries": entries}, open(out_json, "w"), indent=1)
 
 
+def _per_class(csv_path: str):
+    """{class: {counter: sum over dispatches, 'dur': seconds, 'n': dispatches}}."""
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(csv_path)):
+        d = per[int(r["Dispatch_Id"])]
+        d["cls"] = kernel_class(r["Kernel_Name"])
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = collections.OrderedDict()
+    for d in per.values():
+        if d["cls"] in ("foreign", "copy"):
+            continue
+        a = agg.setdefault(d["cls"], collections.defaultdict(float))
+        a["n"] += 1
+        for k, v in d.items():
+            if k != "cls":
+                a[k] += v
+    return agg
+
+
+# gfx950 reports GRBM_GUI_ACTIVE summed over its 8 XCDs; 256 CUs, 1024 SIMDs
+_XCD, _CU, _SIMD = 8, 256, 1024
+
+
+def counters(out_md: str, title: str, pairs) -> None:
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("Clock = GRBM_GUI_ACTIVE per XCD / kernel duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                "(cycles x 1024 SIMDs); MFMA rate = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop / duration; "
+                "LDS read = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 B / (cycles x 256 CUs); waits as a fraction of "
+                "SQ_WAVE_CYCLES.  Averages over the profiled launches.\n\n")
+        for csv_path, command in pairs:
+            agg = _per_class(csv_path)
+            f.write(f"## `{command}`\n\n")
+            f.write("| kernel class | launches | avg ms | clock GHz | MFMA busy | MFMA TFLOP/s | LDS read B/clk/CU | "
+                    "wait any | wait LDS |\n|---|---|---|---|---|---|---|---|---|\n")
+            for cls, a in agg.items():
+                g = a.get("GRBM_GUI_ACTIVE", 0.0) / _XCD
+                dur = a["dur"]
+                def pct(key, denom):
+                    return f"{100.0 * a[key] / denom:.1f}%" if key in a and denom > 0 else "-"
+                clk = f"{g / dur / 1e9:.2f}" if g else "-"
+                mfma = pct("SQ_VALU_MFMA_BUSY_CYCLES", g * _SIMD)
+                rate = (f"{a['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / dur / 1e12:.0f}"
+                        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in a else "-")
+                lds = (f"{a['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / (g * _CU):.1f}"
+                       if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in a and g else "-")
+                wa = pct("SQ_WAIT_ANY", a.get("SQ_WAVE_CYCLES", 0.0))
+                wl = pct("SQ_WAIT_INST_LDS", a.get("SQ_WAVE_CYCLES", 0.0))
+                f.write(f"| {cls} | {int(a['n'])} | {dur * 1e3 / a['n']:.3f} | {clk} | {mfma} | {rate} | {lds} | "
+                        f"{wa} | {wl} |\n")
+            f.write("\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "counters":
+        rest = sys.argv[4:]
+        counters(sys.argv[2], sys.argv[3], [(rest[i], rest[i + 1]) for i in range(0, len(rest), 2)])
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], int(sys.argv[7]))
     else:
