@@ -777,7 +777,7 @@ __global__ void cast_f32_bf16_kernel(const float* __restrict__ src, bf16_t* __re
 // and writes
 //   G [t - tb0][v - vb0]  (row stride ldG)  and  Gt[v - vb0][t - tb0] (ldGt)
 // with G = s_t (M_t q_t[v] - p~_t[v]); rows t >= T and columns v >= V get 0.
-// bf16 may pass Gt = null: G alone is written.
+// bf16 writes G alone (Gt must be null: its contractions read G k-major).
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
     const typename C::TIn* __restrict__ H, const typename C::TIn* __restrict__ W, int T, int d, int V, int K,
@@ -788,12 +788,13 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   using TIn = typename C::TIn;
   // bf16 256 x 256 tiles leave the kernel through the LDS (the whole tile,
   // 128 KiB, once the main loop is done with it) as 16-byte stores that
-  // form 512-byte runs of G rows (and of G^T rows when Gt is not null);
-  // otherwise straight from registers.  Staging also frees the registers the
-  // substep pipeline of the main loop needs.
+  // form 512-byte runs of G rows; otherwise straight from registers.
+  // Staging also frees the registers the substep pipeline of the main loop
+  // needs.
   constexpr bool kStage = std::is_same<TIn, bf16_t>::value && C::BM == 256 && C::BN == 256 && C::WM == 128 &&
-                          C::LDS_BYTES >= 256 * 256 * 2;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+                          C::LDS_BYTES >= 256 * 256 * 2 && PrefetchOK<C>::value;
+  // after the stages: the row constants and the teacher walk's slots (below)
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES + C::BN * 16 + C::NB * C::NTHREADS * 8];
   uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
   // 16-byte chunk c of token row t sits at c ^ (t / 8): the column reads of
   // eight consecutive rows spread over the banks
@@ -813,67 +814,130 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
   const int vt0 = split * tiles_per_split;
   const int vt1 = min(n_vtiles, vt0 + tiles_per_split);
 
-  // Per-lane token state kept across tiles: only the teacher cursor.  The
-  // per-row scale, mass and LSE are re-read for every tile (cached loads),
-  // which keeps registers free for the accumulators.
+  // Row constants of the block's BN token rows, read by every tile's
+  // epilogue from LDS (after the main loop's stages): (s M, LSE log2e, s).
+  // Rows past T and rows of zero scale get (0, +inf, 0), which makes their g
+  // exactly zero (their logits are finite: operand rows past T load as zeros).
+  float4* s_row = reinterpret_cast<float4*>(smem + C::LDS_BYTES);
+  // Teacher walk, one cursor per lane and column block: position cur of the
+  // next teacher entry nxt at or after the tile's first row (registers), and
+  // that entry's p and the index after it in LDS, refilled by global->LDS
+  // loads after the tile that moved the cursor, so that an epilogue with at
+  // most one hit per token waits for no global load.
+  int* s_nx = reinterpret_cast<int*>(smem + C::LDS_BYTES + C::BN * sizeof(float4));  // [NB][NTHREADS]
+  float* s_pc = reinterpret_cast<float*>(s_nx + C::NB * C::NTHREADS);                 // [NB][NTHREADS]
+  for (int i = threadIdx.x; i < C::BN; i += C::NTHREADS) {
+    const int tok = t0 + i;
+    float4 rc = make_float4(0.f, INFINITY, 0.f, 0.f);
+    if (tok < T) {
+      const float sc = srow[tok];
+      if (sc != 0.f) rc = make_float4(sc * Mrow[tok], lse[tok] * kLog2e, sc, 0.f);
+    }
+    s_row[i] = rc;
+  }
   int cur[C::NB], nxt[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     const int tok = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
     cur[nb] = K;
     nxt[nb] = kIdxEnd;
+    int nx = kIdxEnd;
+    float pc = 0.f;
     if (tok < T) {
       const int* row = idx_s + (int64_t)tok * K;
       cur[nb] = lower_bound_row(row, K, vb0 + vt0 * C::BM);
-      nxt[nb] = cur[nb] < K ? row[cur[nb]] : kIdxEnd;
+      if (cur[nb] < K) {
+        nxt[nb] = row[cur[nb]];
+        pc = p_s[(int64_t)tok * K + cur[nb]];
+      }
+      if (cur[nb] + 1 < K) nx = row[cur[nb] + 1];
     }
+    s_nx[nb * C::NTHREADS + threadIdx.x] = nx;
+    s_pc[nb * C::NTHREADS + threadIdx.x] = pc;
   }
+  __syncthreads();
 
+  // The slots of the lanes whose cursor moved in a tile are refilled after
+  // that tile's LDS work (p of entry cur, index of entry cur + 1; a slot
+  // past the list is never read: the walk stops at K), by global->LDS loads
+  // that the next tile's main loop waits for.
+  auto refill = [&](int moved) {
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+      if (moved & (1 << nb)) {
+        const int64_t e = (int64_t)(t0 + wave_n * C::WN + nb * 32 + (lane & 31)) * K + cur[nb];
+        if (cur[nb] < K) lds_dma4(p_s + e, s_pc + nb * C::NTHREADS + wave * 64);
+        if (cur[nb] + 1 < K) lds_dma4(idx_s + e + 1, s_nx + nb * C::NTHREADS + wave * 64);
+      }
+  };
   typename C::TileT tile;
+  if constexpr (kStage)
+    if (vt0 < vt1)
+      tile_k64_prologue<C>(W + (int64_t)(vb0 + vt0 * C::BM) * d, d, V - vb0 - vt0 * C::BM, H + (int64_t)t0 * d, d,
+                           T - t0, d, smem);
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vb0 + vt * C::BM;
-    run_mma(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    if constexpr (kStage) {
+      run_mma<C, true>(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    } else {
+      run_mma(tile, W + (int64_t)v0 * d, d, V - v0, H + (int64_t)t0 * d, d, T - t0, d, smem);
+    }
+    if constexpr (!kStage) wait_vmcnt<0>();  // the slots refilled after the previous tile
     const int vbase = v0 + wave_m * C::WM;
     const int vend = min(v0 + C::BM, V);
+    const bool full = vbase + C::WM <= V;  // every row of the wave's slice is a vocabulary row
+    int moved = 0;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
-      const int tok = t0 + wave_n * C::WN + nb * 32 + (lane & 31);
-      float sc = 0.f, coef = 0.f, lse2 = INFINITY;
-      if (tok < T) {
-        sc = srow[tok];
-        coef = sc * Mrow[tok];
-        // rows with zero scale (masked) give exact zeros whatever their lse
-        if (sc != 0.f) lse2 = lse[tok] * kLog2e;
-      }
+      // (opaque: the addresses derived from it are formed here, not held in
+      // registers across the main loop)
+      const int tl = opaque(wave_n * C::WN + nb * 32 + (lane & 31));
+      const int tok = t0 + tl;
+      const float4 rc = s_row[tl];
+      const float coef = rc.x, lse2 = rc.y;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vbase + mb * 32 + acc_row(r, lane);
-          const float z = tile.acc[mb][nb][r];
-          const float g = coef * fast_exp2(z * kLog2e - lse2);
-          tile.acc[mb][nb][r] = (v < V && tok < T) ? g : 0.f;
-        }
-      while (nxt[nb] < vend) {
-        const int vl = nxt[nb] - vbase;
-        if (vl >= 0 && vl < C::WM) {
+        for (int r = 0; r < 16; ++r) tile.acc[mb][nb][r] = coef * fast_exp2(tile.acc[mb][nb][r] * kLog2e - lse2);
+      if (!full) {  // the last tile: columns v >= V (zero operand rows) get 0
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vbase + mb * 32 + acc_row(r, lane) >= V) tile.acc[mb][nb][r] = 0.f;
+      }
+      int ccur = cur[nb], cnxt = nxt[nb];
+      if (cnxt < vend) {
+        const int slot = nb * C::NTHREADS + threadIdx.x;
+        float pc = s_pc[slot];  // p of entry ccur
+        int nx = s_nx[slot];    // index of entry ccur + 1
+        do {
+          // entry ccur (index cnxt) lies in this tile: subtract s p at its
+          // register (in the lane of the right half of the 32-row block)
+          const int vl = cnxt - vbase;
           const int rr = vl & 31;
-          if (((rr >> 2) & 1) == (lane >> 5)) {
+          if (vl >= 0 && vl < C::WM && ((rr >> 2) & 1) == (lane >> 5)) {
             const int sel = (vl >> 5) * 16 + (rr >> 3) * 4 + (rr & 3);
-            const float sp = sc * p_s[(int64_t)tok * K + cur[nb]];
+            const float sp = rc.z * pc;
 #pragma unroll
             for (int q = 0; q < C::MB * 16; ++q)
               if (q == sel) tile.acc[q / 16][nb][q % 16] -= sp;
           }
-        }
-        ++cur[nb];
-        nxt[nb] = cur[nb] < K ? idx_s[(int64_t)tok * K + cur[nb]] : kIdxEnd;
+          ++ccur;
+          cnxt = ccur < K ? nx : kIdxEnd;
+          if (cnxt < vend) {  // another entry in this tile (rare): read the list directly
+            pc = p_s[(int64_t)tok * K + ccur];
+            nx = ccur + 1 < K ? idx_s[(int64_t)tok * K + ccur + 1] : kIdxEnd;
+          }
+        } while (cnxt < vend);
+        cur[nb] = ccur;
+        nxt[nb] = cnxt;
+        moved |= 1 << nb;
       }
       if constexpr (kStage) {
         // g of this lane's token column into the LDS tile [t][v]: registers
         // 4i .. 4i + 3 hold vocabulary rows 8i + 4 (lane / 32) .. + 3, one
         // 8-byte half of the 16-byte chunk (wave_m 16 + mb 4 + i)
-        const int tl = wave_n * C::WN + nb * 32 + (lane & 31);
         uint2* row = reinterpret_cast<uint2*>(stg + tl * 256);
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb)
@@ -909,41 +973,32 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_grad_kernel(
       }
     }
     if constexpr (kStage) {
+      // G rows: 32 threads per token row of 256 entries (512 bytes).  The
+      // tile is read out of the LDS into registers first, so that the next
+      // tile's first two slices go into the stages before the stores are
+      // issued: their latencies overlap, and the next loop waits for both.
       __syncthreads();
-      const int tid = threadIdx.x;
-      bf16_t* Gtile = G + (int64_t)(t0 - tb0) * ldG + (v0 - vb0);
-      // (offset of the G^T tile; a pointer is formed only when there is a G^T)
-      const int64_t gt_origin = (int64_t)(v0 - vb0) * ldGt + (t0 - tb0);
-      // G rows: 32 threads per token row of 256 entries (512 bytes)
-#pragma unroll 2
-      for (int pass = 0; pass < 256 / (C::NTHREADS / 32); ++pass) {
+      const int tid = opaque(threadIdx.x);  // (addresses formed here, not held across the loop)
+      constexpr int kPasses = 256 / (C::NTHREADS / 32);
+      u32x4 out[kPasses];
+#pragma unroll
+      for (int pass = 0; pass < kPasses; ++pass) {
         const int tl = pass * (C::NTHREADS / 32) + (tid >> 5), q = tid & 31;
-        const u32x4 v = reinterpret_cast<const u32x4*>(stg + tl * 256)[stage_chunk(tl, q)];
-        *reinterpret_cast<u32x4*>(Gtile + (int64_t)tl * ldG + q * 8) = v;
+        out[pass] = reinterpret_cast<const u32x4*>(stg + tl * 256)[stage_chunk(tl, q)];
       }
-      // G^T rows (when asked for): an 8 x 8 block (tokens 8 tq .., vocabulary
-      // 8 vb ..) per thread and pass, transposed in registers; 32 threads
-      // write one vocabulary row's 512 bytes
-#pragma unroll 1
-      for (int pass = 0; pass < (Gt != nullptr ? 1024 / C::NTHREADS : 0); ++pass) {
-        const int blk = pass * C::NTHREADS + tid, tq = blk & 31, vb = blk >> 5;
-        u32x4 a[8];
+      __syncthreads();
+      if (vt + 1 < vt1)
+        tile_k64_prologue<C>(W + (int64_t)(v0 + C::BM) * d, d, V - v0 - C::BM, H + (int64_t)t0 * d, d, T - t0, d,
+                             smem);
+      refill(moved);
+      bf16_t* Gtile = G + (int64_t)(t0 - tb0) * ldG + (v0 - vb0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = reinterpret_cast<const u32x4*>(stg + (tq * 8 + i) * 256)[vb ^ tq];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // vocabulary rows 2w (low halves) and 2w + 1 (high halves)
-          u32x4 lo, hi;
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) {
-            lo[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x05040100u);
-            hi[i2] = __builtin_amdgcn_perm(a[2 * i2 + 1][w], a[2 * i2][w], 0x07060302u);
-          }
-          bf16_t* gt = Gt + gt_origin + (int64_t)(vb * 8 + 2 * w) * ldGt + tq * 8;
-          *reinterpret_cast<u32x4*>(gt) = lo;
-          *reinterpret_cast<u32x4*>(gt + ldGt) = hi;
-        }
+      for (int pass = 0; pass < kPasses; ++pass) {
+        const int tl = pass * (C::NTHREADS / 32) + (tid >> 5), q = tid & 31;
+        *reinterpret_cast<u32x4*>(Gtile + (int64_t)tl * ldG + q * 8) = out[pass];
       }
-      __syncthreads();  // the next tile's loads refill the LDS
+    } else {
+      refill(moved);
     }
   }
 }
@@ -1678,6 +1733,7 @@ static hipError_t bwd_grad_t(const void* H, const void* W, int T, int d, int V, 
                              int t_rows, int vb0, int v_rows, int n_splits, int tiles_per_split, void* G,
                              int64_t ldG, void* Gt, int64_t ldGt, const int* nrows, hipStream_t st) {
   using C = typename CfgOf<TIn>::bwd;
+  if (sizeof(TIn) == 2 && Gt != nullptr) return hipErrorInvalidValue;  // bf16 forms G only
   const int n_vtiles = v_rows / C::BM;
   const int n_tblocks = t_rows / C::BN;
   hipLaunchKernelGGL(bwd_grad_kernel<C>, dim3(n_tblocks * n_splits), dim3(C::NTHREADS), 0, st, (const TIn*)H,
