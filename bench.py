@@ -258,6 +258,7 @@ def run(args) -> dict:
     torch.cuda.set_device(dev)
     torch.empty(1, device=dev)  # initialise the context before resetting the peak counter
     torch.cuda.reset_peak_memory_stats(dev)
+    free0 = torch.cuda.mem_get_info(dev)[0]  # device memory free before the inputs (hipMemGetInfo)
     H, W, idx, tl, mask = upload(x, dev)
     T, d, V, K = x.T, x.d, x.V, x.K
     n_kept = int(T if x.mask is None else x.mask.sum())
@@ -317,7 +318,8 @@ def run(args) -> dict:
             del got
             rl = None  # the timed steps do not write the row losses
             torch.cuda.synchronize(dev)
-            # the parity check's host copies are not part of a step's footprint
+            # the parity check's copies are not part of a step's footprint
+            torch.cuda.empty_cache()
             torch.cuda.reset_peak_memory_stats(dev)
             fwd()
             bwd()
@@ -339,6 +341,10 @@ def run(args) -> dict:
         bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
         step_ms = wall * 1e3 / steps
         peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+        # what the driver sees in use (hipMemGetInfo): inputs, outputs, the
+        # workspaces as torch's allocator holds them, the library's code and
+        # its static device array, against the free memory before the inputs
+        used_gib = (free0 - torch.cuda.mem_get_info(dev)[0]) / 2**30
         log(f"timed {steps} steps, path {path}: {step_ms:.2f} ms/step")
         # per-kernel pass: the same steps again with the library's events on
         kt = None
@@ -352,9 +358,13 @@ def run(args) -> dict:
             ckl.timing_enable(False)
         del ws_f, ws_b, dH, dW, loss, lse, row_loss
         torch.cuda.empty_cache()
-        return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, kt=kt, parity=parity,
+        return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, used_gib=used_gib, kt=kt,
+                    parity=parity,
                     fwd_ms=None if fused else float(np.mean(fwd_ms)),
                     bwd_ms=None if fused else float(np.mean(bwd_ms)),
+                    fwd_ms_min=None if fused else float(np.min(fwd_ms)),
+                    bwd_ms_min=None if fused else float(np.min(bwd_ms)),
+                    events_mean_ms=float(np.mean(np.add(fwd_ms, bwd_ms))),
                     events_min_ms=float(np.min(np.add(fwd_ms, bwd_ms))))
 
     m = measure(args.path, args.steps, args.warmup, check=args.parity)
@@ -419,8 +429,12 @@ def run(args) -> dict:
         "tflops_multiplied": flops_mult / (step_ms * 1e-3) / 1e12,
         "pct_bf16_peak": 100.0 * flops_mult / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "peak_hbm_gib": m["peak_gib"],
+        "hbm_in_use_gib_mem_get_info": m["used_gib"],
         "fwd_ms": m["fwd_ms"],
         "bwd_ms": m["bwd_ms"],
+        "fwd_ms_min": m["fwd_ms_min"],
+        "bwd_ms_min": m["bwd_ms_min"],
+        "step_ms_events_mean": m["events_mean_ms"],
         "step_ms_events_min": m["events_min_ms"],
         "parity": m["parity"],
         "kernels": kernels,
@@ -431,7 +445,10 @@ def run(args) -> dict:
         other = "recompute" if fused else "fused"
         o = measure(other, args.steps, args.warmup, check=False)
         result["other_path"] = {"path": other, "ms_per_step": o["step_ms"], "tokens_per_s": T / (o["step_ms"] * 1e-3),
-                                "peak_hbm_gib": o["peak_gib"], "fwd_ms": o["fwd_ms"], "bwd_ms": o["bwd_ms"],
+                                "peak_hbm_gib": o["peak_gib"], "hbm_in_use_gib_mem_get_info": o["used_gib"],
+                                "fwd_ms": o["fwd_ms"], "bwd_ms": o["bwd_ms"],
+                                "fwd_ms_min": o["fwd_ms_min"], "bwd_ms_min": o["bwd_ms_min"],
+                                "step_ms_events_min": o["events_min_ms"],
                                 "tflops_multiplied": (6.0 if other == "fused" else 8.0) * rows_mult * V * d
                                 / (o["step_ms"] * 1e-3) / 1e12,
                                 "plan": o["plan"],
@@ -491,6 +508,9 @@ def matrix(args) -> dict:
                          "ms_per_step": row["ms_per_step"], "tokens_per_s": row["value"],
                          "tflops_useful": row["tflops"], "tflops_multiplied": row["tflops_multiplied"],
                          "pct_bf16_peak": row["pct_bf16_peak"], "peak_hbm_gib": row["peak_hbm_gib"],
+                         "hbm_in_use_gib_mem_get_info": row["hbm_in_use_gib_mem_get_info"],
+                         "fwd_ms": row["fwd_ms"], "bwd_ms": row["bwd_ms"], "fwd_ms_min": row["fwd_ms_min"],
+                         "bwd_ms_min": row["bwd_ms_min"], "step_ms_events_min": row["step_ms_events_min"],
                          "parity": row["parity"], "wall_s": time.perf_counter() - t0})
             log(f"  {row['ms_per_step']:.1f} ms/step, peak {row['peak_hbm_gib']:.2f} GiB, "
                 f"parity {'pass' if row['parity'] and row['parity']['pass'] else 'FAIL'}")
