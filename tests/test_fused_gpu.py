@@ -76,6 +76,9 @@ def test_fused_chunk_sizes(chunk):
     (257, 136, 129, 5, "bf16"),
     (64, 4096, 4096, 64, "bf16"),
     (300, 40, 777, 13, "f32"),
+    (40, 64, 5000, 4096, "bf16"),  # K at its maximum
+    (300, 64, 9000, 2, "bf16"),    # a short teacher list ending early in a long vocabulary walk
+    (17, 16384, 700, 5, "bf16"),   # 16K hidden size
 ])
 def test_fused_edge_shapes(T, d, V, K, dtype):
     x = _custom(T, d, V, K, dtype)

@@ -140,6 +140,9 @@ def _custom(T, d, V, K, dtype="bf16", seed=5, mask=None, tscale=1.0):
     (130, 24, 300, 300, "bf16"),  # K = V: full-support teacher; ragged rows
     (257, 136, 129, 5, "bf16"),   # everything one past a tile boundary
     (64, 4096, 4096, 64, "bf16"), # long hidden size
+    (40, 64, 5000, 4096, "bf16"), # K at its maximum (4096 teacher entries per row)
+    (300, 64, 9000, 2, "bf16"),   # a short teacher list ending early in a long vocabulary walk
+    (17, 16384, 700, 5, "bf16"),  # 16K hidden size (256 k slices per tile)
 ])
 def test_edge_shapes(T, d, V, K, dtype):
     x = _custom(T, d, V, K, dtype)
