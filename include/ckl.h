@@ -38,7 +38,9 @@
  * Device arrays must be 16-byte aligned.
  *
  * Ownership.  The caller allocates every buffer, the workspace included.  The
- * library allocates no device memory, keeps no state between calls (apart from
+ * library allocates no device memory at run time (its one device allocation is
+ * a 64 MiB static array that comes with its code on every GPU it runs on, the
+ * workspace of ckl_forward_noalloc), keeps no state between calls (apart from
  * the optional timing records, see ckl_timing_enable) and holds no pointer
  * after a call returns (apart from work queued on `stream`).
  *
@@ -293,7 +295,7 @@ typedef enum {
  * every kernel the library launches is bracketed by two hipEvents recorded on
  * the launch stream; enabling (again) clears the accumulated records, on = 0
  * stops recording.  Process-wide; the records are the only state the library
- * keeps between calls, and the events are its only allocations. */
+ * keeps between calls, and the events are its only run-time allocations. */
 ckl_status ckl_timing_enable(int on);
 
 /* Waits for the recorded events, adds their durations to the totals of each
