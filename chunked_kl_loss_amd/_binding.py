@@ -190,6 +190,23 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
 
 
+# Checking aid: a byte value (0..255) with which every workspace and output
+# buffer the functions below allocate is filled before the library call, so
+# that a result depending on memory the library should have written (the
+# workspace contents on entry do not matter, outputs are overwritten) shows up:
+# 0xFF makes float32 and bf16 words NaN.  None (the default): plain
+# torch.empty, nothing filled.
+FILL_BYTE = None
+
+
+def _empty(shape, dtype, device):
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if FILL_BYTE is not None and t.numel() > 0:
+        t.view(torch.uint8).fill_(int(FILL_BYTE))
+    return t
+
+
 def _torch_dtype(code: int):
     torch = _torch()
     return torch.bfloat16 if code == CKL_BF16 else torch.float32
@@ -236,10 +253,10 @@ def forward(H, W, idx, tlogit, mask=None, chunk: int = 2048, validate: bool = Fa
     lib = load_library()
     ws_bytes = workspace_size(prob, 0)
     dev = H.device
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(T, dtype=torch.float32, device=dev)
-    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    ws = _empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = _empty(1, dtype=torch.float32, device=dev)
+    lse = _empty(T, dtype=torch.float32, device=dev)
+    row_loss = _empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
     m = mask.view(torch.uint8) if mask is not None else None
     check(lib.ckl_forward(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlogit), _ptr(m),
                           _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
@@ -262,9 +279,9 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     lib = load_library()
     ws_bytes = workspace_size(prob, 1)
     dev = H.device
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    dH = torch.empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
-    dW = torch.empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
+    ws = _empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dH = _empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
+    dW = _empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
     m = mask.view(torch.uint8) if mask is not None else None
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
@@ -291,12 +308,12 @@ def forward_backward(H, W, idx, tlogit, mask=None, grad_loss=None, chunk: int = 
     lib = load_library()
     ws_bytes = workspace_size(prob, 2)
     dev = H.device
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(T, dtype=torch.float32, device=dev)
-    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
-    dH = torch.empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
-    dW = torch.empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
+    ws = _empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = _empty(1, dtype=torch.float32, device=dev)
+    lse = _empty(T, dtype=torch.float32, device=dev)
+    row_loss = _empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    dH = _empty((T, d), dtype=_torch_dtype(dh_code), device=dev)
+    dW = _empty((V, d), dtype=_torch_dtype(dw_code), device=dev)
     m = mask.view(torch.uint8) if mask is not None else None
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
@@ -319,9 +336,9 @@ def shard_forward(H, W_shard, idx, tlogit, v_offset: int, v_total: int, chunk: i
     lib = load_library()
     ws_bytes = workspace_size(prob, 0)
     dev = H.device
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    lse_part = torch.empty(T, dtype=torch.float32, device=dev)
-    cross_part = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = _empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    lse_part = _empty(T, dtype=torch.float32, device=dev)
+    cross_part = _empty(T, dtype=torch.float32, device=dev)
     check(lib.ckl_shard_forward(ctypes.byref(prob), _ptr(H), _ptr(W_shard), _ptr(idx), _ptr(tlogit),
                                 _ptr(lse_part), _ptr(cross_part), _ptr(ws), ws_bytes, _stream_ptr(dev)), lib)
     return lse_part, cross_part
@@ -340,10 +357,10 @@ def shard_combine(lse_parts, cross_parts, idx, tlogit, mask=None, v_total: int =
     lib = load_library()
     ws_bytes = workspace_size(prob, 3)
     dev = lse_parts.device
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(T, dtype=torch.float32, device=dev)
-    row_loss = torch.empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
+    ws = _empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = _empty(1, dtype=torch.float32, device=dev)
+    lse = _empty(T, dtype=torch.float32, device=dev)
+    row_loss = _empty(T, dtype=torch.float32, device=dev) if want_row_loss else None
     m = mask.view(torch.uint8) if mask is not None else None
     check(lib.ckl_shard_combine(ctypes.byref(prob), int(n_shards), _ptr(lse_parts), _ptr(cross_parts), _ptr(idx),
                                 _ptr(tlogit), _ptr(m), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws_bytes,

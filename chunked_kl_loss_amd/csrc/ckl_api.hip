@@ -251,7 +251,9 @@ Plan make_plan(const ckl_problem* p) {
   const int64_t sh_max = std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, q.Vp / 256));
   int64_t best_cost = -1;
   for (int64_t sh = 1; sh <= sh_max; ++sh) {
-    const int64_t vs = round_up(ceil_div(q.Vp, sh), 256);
+    // (at most Vp: fp32 pads the vocabulary to 128 columns, and a part may
+    // not reach into the row padding of G and W^T past it)
+    const int64_t vs = std::min(round_up(ceil_div(q.Vp, sh), 256), q.Vp);
     const int64_t parts = ceil_div(q.Vp, vs);
     if (parts != sh) continue;  // the same split as a smaller count
     const int64_t cost = ceil_div(dh_tiles * parts, kCUs) * (vs + kEpilogueK);

@@ -11,6 +11,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running (minutes of CPU oracle work)")
+    # every workspace and output buffer the binding allocates starts as 0xFF
+    # bytes (NaN words): a result that reads memory the library did not write
+    # first fails its comparison instead of passing on zeroed memory
+    import chunked_kl_loss_amd._binding as binding
+    binding.FILL_BYTE = 0xFF
 
 
 def _has_gpu():
