@@ -11,7 +11,9 @@ element against the oracle, to the tolerances of the other parity tests
 2e-3 absolute; fp32: 1e-5; bf16 gradient outputs: 1e-2).  A wider draw adds
 larger problems, bf16 gradient outputs, the device index check and the
 one-call path's dW-group budget; a third draws ragged vocabulary shards
-(ckl_shard_forward, ckl_shard_combine, ckl_backward per shard).  The seed
+(ckl_shard_forward, ckl_shard_combine, ckl_backward per shard); a fourth
+draws problems of up to 12K rows and 70K vocabulary rows, large enough for
+plans with several G blocks, dH split parts and dW groups.  The seed
 lists are fixed, so a failure names a reproducible problem; every buffer the
 binding allocates starts as NaN bytes (tests/conftest.py).
 """
@@ -125,3 +127,35 @@ def test_drawn_vocabulary_shards(seed):
     ref = oracle_full(x, grad_loss=c["grad_loss"], teacher_form=c["teacher_form"])
     got = run_shards(x, bounds, grad_loss=c["grad_loss"], chunk=c["chunk"], teacher_form=c["teacher_form"])
     check_shards(x, got, ref, TOL[c["dtype"]], 2e-3 if c["dtype"] == "bf16" else 1e-5)
+
+
+def draw_large(seed):
+    """Problems large enough for multi-block plans: several G blocks in both
+    directions, dH split parts, several dW groups, many vocabulary splits."""
+    rng = np.random.default_rng(9000 + seed)
+    T = int(rng.integers(2000, 12000))
+    V = int(rng.integers(20000, 70000))
+    mask = (rng.random(T) < rng.uniform(0.3, 0.95)).astype(np.uint8) if rng.random() < 0.5 else None
+    return dict(dtype="f32" if rng.random() < 0.2 else "bf16", T=T, d=8 * int(rng.integers(8, 65)), V=V,
+                K=int(rng.integers(1, 201)), chunk=int(rng.choice([256, 512, 1024, 2048, 4096])), mask=mask,
+                compact=bool(rng.random() < 0.5), teacher_form=int(rng.random() < 0.25),
+                grad_loss=float(rng.choice([1.0, 0.5, -2.0])))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_drawn_large_problem(seed):
+    c = draw_large(seed)
+    x = _custom(c["T"], c["d"], c["V"], c["K"], c["dtype"], seed=seed + 13)
+    if c["teacher_form"]:
+        x = with_logprob_teacher(x, seed=seed)
+    kept = c["T"] if c["mask"] is None else int(c["mask"].sum())
+    say(f"case drawn large seed={seed} T={c['T']} d={c['d']} V={c['V']} K={c['K']} chunk={c['chunk']} "
+        f"{c['dtype']} kept={kept} compact={c['compact']} teacher_form={c['teacher_form']} "
+        f"grad_loss={c['grad_loss']}")
+    ref = oracle_full(x, grad_loss=c["grad_loss"], mask=c["mask"], teacher_form=c["teacher_form"])
+    tol = TOL[c["dtype"]]
+    lse_tol = 2e-3 if c["dtype"] == "bf16" else 1e-5
+    args = dict(chunk=c["chunk"], grad_loss=c["grad_loss"], mask=c["mask"], teacher_form=c["teacher_form"],
+                compact=c["compact"])
+    check_full(x, run_gpu(x, **args), ref, tol, lse_tol)
+    check_full(x, run_gpu_fused(x, **args), ref, tol, lse_tol)
