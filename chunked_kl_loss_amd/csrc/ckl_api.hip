@@ -326,7 +326,8 @@ BwdWs bwd_layout(const Plan& q, const ckl_problem* p) {
   w.N = take(4);
   w.bad = take(4);
   w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
-  w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
+  // W^T of one vocabulary block at a time (the blocks are the outer loop)
+  w.Wt = take((size_t)q.d * (q.Vc + kLdPad) * q.esz);
   // bf16 keeps G only (the dW contraction reads it k-major); fp32 also G^T
   for (int i = 0; i < kGBuffers; ++i) {
     w.G[i] = take((size_t)q.Tc * (q.Vc + kLdPad) * q.esz);
@@ -679,15 +680,19 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
                 [&] { return ckl::launch_transpose_pad(q.in_bf16, Hs, T, d, (int)q.Tp, Ht, q.Tp + kLdPad, st); }),
           "transpose H");
-  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, q.Vp + kLdPad, st); }),
-          "transpose W");
 
   const char* Htb = (const char*)Ht;
-  const char* Wtb = (const char*)Wt;
+  const int64_t ldWt = q.Vc + kLdPad;
   for (int64_t vb = 0; vb < q.nV; ++vb) {
     const int64_t vb0 = vb * q.Vc;
     const int64_t vrows = std::min(q.Vc, q.Vp - vb0);
+    // W^T of this vocabulary block (zero columns past V)
+    HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                  [&] {
+                    return ckl::launch_transpose_pad(q.in_bf16, (const char*)W + vb0 * q.d * q.esz,
+                                                     (int)std::min(q.Vc, q.V - vb0), d, (int)vrows, Wt, ldWt, st);
+                  }),
+            "transpose W block");
     for (int64_t tb = 0; tb < q.nT; ++tb) {
       const int64_t tb0 = tb * q.Tc;
       const int64_t trows = std::min(q.Tc, q.Tp - tb0);
@@ -708,7 +713,7 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
       ckl::GemmArgs gdw{q.in_bf16 ? G : Gt, q.in_bf16 ? vrows + kLdPad : trows + kLdPad, Htb + tb0 * q.esz,
                         q.Tp + kLdPad, dWacc + vb0 * q.d, q.d, (int)std::min(vrows, q.V - vb0), d, (int)trows, tb > 0};
       gdw.xt = q.in_bf16;
-      ckl::GemmArgs gdh{G, vrows + kLdPad, Wtb + vb0 * q.esz, q.Vp + kLdPad, dHacc + tb0 * q.d, q.d,
+      ckl::GemmArgs gdh{G, vrows + kLdPad, Wt, ldWt, dHacc + tb0 * q.d, q.d,
                         (int)std::min(trows, q.T - tb0), d, (int)vrows, vb > 0};
       if (pk.on()) {
         // packed rows: the token rows of this block past the kept rows are
