@@ -35,7 +35,7 @@ def _both(x, chunk, packed=False):
             status = lib.ckl_forward_noalloc(ctypes.byref(prob), H.data_ptr(), W.data_ptr(), idx.data_ptr(),
                                              tl.data_ptr(), mp, loss.data_ptr(), lse.data_ptr(), rl.data_ptr(), st)
         else:
-            ws = torch.empty(B.workspace_size(prob, 0), dtype=torch.uint8, device="cuda")
+            ws = torch.full((B.workspace_size(prob, 0),), 0xFF, dtype=torch.uint8, device="cuda")
             status = lib.ckl_forward(ctypes.byref(prob), H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(),
                                      mp, loss.data_ptr(), lse.data_ptr(), rl.data_ptr(), ws.data_ptr(), ws.numel(),
                                      st)
@@ -54,6 +54,22 @@ def test_noalloc_forward_matches_workspace_forward(packed):
         (l0, s0, r0), (l1, s1, r1) = _both(x, chunk, packed)
         assert np.isfinite(l0).all() and np.isfinite(s0).all() and np.isfinite(r0).all()
         assert np.array_equal(l0, l1) and np.array_equal(s0, s1) and np.array_equal(r0, r1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_noalloc_forward_drawn(seed):
+    # drawn problems (dtype, shapes, chunk, mask with or without packing)
+    import dataclasses
+
+    from tests.test_parity_gpu import _custom
+    from tests.test_random_shapes_gpu import draw
+    c = draw(seed + 300)
+    x = dataclasses.replace(_custom(c["T"], c["d"], c["V"], c["K"], c["dtype"], seed=seed), mask=c["mask"])
+    say(f"case no-alloc forward drawn seed={seed} T={x.T} d={x.d} V={x.V} K={x.K} chunk={c['chunk']} "
+        f"{x.dtype} masked={x.mask is not None} packed={c['compact']}")
+    (l0, s0, r0), (l1, s1, r1) = _both(x, c["chunk"], c["compact"])
+    assert np.isfinite(l0).all() and np.isfinite(s0).all() and np.isfinite(r0).all()
+    assert np.array_equal(l0, l1) and np.array_equal(s0, s1) and np.array_equal(r0, r1)
 
 
 def test_noalloc_forward_unmasked_fp32():
