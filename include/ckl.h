@@ -189,8 +189,9 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W,
  * blocks held at once (each stored as G [Tc, Vc], and for fp32 also its
  * transpose; the two layouts' budget together is about chunk * V
  * elements).  dW is read-modified-
- * written once per extra token block and dH once per extra vocabulary block.
- * Host-only; touches no device. */
+ * written once per extra token block and dH once per extra vocabulary block;
+ * the vocabulary blocks are the outer loop, and W^T is staged for one block
+ * at a time ([d, Vc] in the workspace).  Host-only; touches no device. */
 ckl_status ckl_backward_plan(const ckl_problem* p, int64_t out[5]);
 
 /* Forward and backward in one call, without recomputing the logits.
