@@ -363,7 +363,8 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   w.N = take(4);
   w.bad = take(4);
   w.s = take(q.Tp * 4);
-  w.Ht = take((size_t)q.d * (q.Tp + kLdPad) * q.esz);
+  // H^T of one dW group's rows at a time (its update reads no other rows)
+  w.Ht = take((size_t)q.d * (q.Gc * q.Cs + kLdPad) * q.esz);
   w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
   // bf16: u of a chunk in the forward's tile order, laid out as G and G^T
   // by gpass_tiles (fp32 keeps u in G itself)
@@ -779,7 +780,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   float* dHp = (float*)(b + w.dHp);
   float* dWacc = p->dw_dtype == CKL_BF16 ? (float*)(b + w.dW) : (float*)dW;
   const int T = (int)q.T, d = (int)q.d, V = (int)q.V, K = (int)q.K;
-  const int64_t ldG = q.Vp + kLdPad, ldGt = q.Gc * q.Cs + kGtPad, ldW = q.Vp + kLdPad, ldH = q.Tp + kLdPad;
+  const int64_t ldG = q.Vp + kLdPad, ldGt = q.Gc * q.Cs + kGtPad, ldW = q.Vp + kLdPad, ldH = q.Gc * q.Cs + kLdPad;
   const int64_t dh_esz = p->dh_dtype == CKL_BF16 ? 2 : 4;
   const Packed pk = (p->compact_mask && mask) ? packed_at(b, w.pk) : Packed{};
   const void* Hs = H;
@@ -811,9 +812,6 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
                 [&] { return ckl::launch_row_scale(mk, grad_loss, N, T, (int)q.Tp, pk.on(), srow, st); }),
           "row_scale");
   HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
-                [&] { return ckl::launch_transpose_pad(q.in_bf16, Hs, T, d, (int)q.Tp, Ht, ldH, st); }),
-          "transpose H");
-  HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
                 [&] { return ckl::launch_transpose_pad(q.in_bf16, W, V, d, (int)q.Vp, Wt, ldW, st); }),
           "transpose W");
 
@@ -827,6 +825,14 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     char* Gtc = q.in_bf16 ? nullptr : Gt + slot * q.Cs * q.esz;
     const bool dw_now = slot == q.Gc - 1 || c == q.nS - 1;       // the group's last chunk
     const char* Hc = (const char*)Hs + tb0 * q.d * q.esz;
+    if (slot == 0) {
+      // H^T of this dW group's rows (zero columns past T); the previous
+      // group's update, which read the buffer, is ahead on the stream
+      const int64_t grows = std::min(q.Gc * q.Cs, q.T - tb0), grows_p = std::min(q.Gc * q.Cs, q.Tp - tb0);
+      HIP_TRY(timed(CKL_KERNEL_TRANSPOSE, st,
+                    [&] { return ckl::launch_transpose_pad(q.in_bf16, Hc, (int)grows, d, (int)grows_p, Ht, ldH, st); }),
+              "transpose H group");
+    }
     HIP_TRY(timed(CKL_KERNEL_FWD_LSE, st,
                   [&] {
                     return ckl::launch_fwd_lse(q.in_bf16, Hc, W, rows, d, V, K, idx_s + tb0 * K, zg_s + tb0 * K,
@@ -868,7 +874,7 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
     const int64_t g0 = c - slot;  // first chunk of the group
     // dW (+)= G^T H over the group's rows: bf16 reads G itself k-major
     // (element (v, t) at G[t ldG + v]), fp32 reads G^T
-    ckl::GemmArgs gdw{q.in_bf16 ? (void*)G : (void*)Gt, q.in_bf16 ? ldG : ldGt, Ht + g0 * q.Cs * q.esz, ldH,
+    ckl::GemmArgs gdw{q.in_bf16 ? (void*)G : (void*)Gt, q.in_bf16 ? ldG : ldGt, Ht, ldH,
                       dWacc, q.d, dw_now ? V : 0, d, (int)(slot * q.Cs + rows_p), g0 > 0};
     gdw.xt = q.in_bf16;
     if (pk.on()) {

@@ -197,7 +197,8 @@ def test_fused_dw_group_budget(lib):
     assert B.fused_plan(prob(1))["dw_group_chunks"] == 1          # at least one chunk
     assert B.fused_plan(prob(1 << 20))["dw_group_chunks"] == 16   # at most every chunk
     saved = B.workspace_size(prob(0), 2) - B.workspace_size(prob(2048), 2)
-    assert saved == pytest.approx(7 * 2048 * (201216 + 128) * 2, rel=1e-3)
+    # seven chunks fewer of G rows and of H^T columns (both staged per group)
+    assert saved == pytest.approx(7 * 2048 * ((201216 + 128) + 2880) * 2, rel=1e-3)
     # at one chunk per group the one-call path holds u and G of one chunk, W^T and
     # the per-row arrays (H^T, the dH split partials, teacher lists)
     chunk_v = 2048 * (201216 + 128) * 2
