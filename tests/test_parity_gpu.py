@@ -206,6 +206,27 @@ def test_bitwise_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_side_stream_matches_default_stream():
+    # every launch and copy of a call goes to the caller's stream: on a
+    # non-default stream (default priority) the results are those of the
+    # default stream, bit for bit, for both paths
+    import torch
+
+    from tests.gpu_harness import run_gpu_fused
+    x = _custom(700, 136, 3000, 40, mask=(np.arange(700) % 3 != 0).astype(np.uint8))
+    say("case non-default stream")
+    a, af = run_gpu(x, chunk=200), run_gpu_fused(x, chunk=200)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b, bf = run_gpu(x, chunk=200), run_gpu_fused(x, chunk=200)
+    torch.cuda.synchronize()
+    for r, q in ((a, b), (af, bf)):
+        assert r["loss"] == q["loss"]
+        for k in ("lse", "row_loss", "dH", "dW"):
+            assert np.array_equal(r[k], q[k]), k
+
+
 def test_autograd_function():
     import torch
 
