@@ -90,3 +90,62 @@ def test_noalloc_forward_limits():
     val = B.make_problem(100, 64, 1000, 8, 64, validate=True)
     st = lib.ckl_forward_noalloc(ctypes.byref(val), fake, fake, fake, fake, None, fake, fake, None, None)
     assert st == B.CKL_ERR_UNSUPPORTED
+
+
+def test_noalloc_forward_under_graph_capture():
+    # the callers this entry point is for: a forward captured into a HIP graph
+    # (torch.cuda.graph) and replayed with new inputs copied into the captured
+    # buffers, eager work and synchronisation between replays; every replay
+    # equals an eager ckl_forward on the same inputs, bit for bit
+    lib = B.load_library()
+    xs = [make_inputs(4, seed=s, T=3000) for s in (7, 8, 9)]   # packed-document masks
+    x0 = xs[0]
+    T, d, V, K = x0.T, x0.d, x0.V, x0.K
+    prob = B.make_problem(T, d, V, K, 256, B.CKL_BF16, compact_mask=True)
+    H, W, idx, tl, m = to_device(x0)
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lse = torch.zeros(T, dtype=torch.float32, device="cuda")
+    rl = torch.zeros(T, dtype=torch.float32, device="cuda")
+
+    def call(use_scratch, ws=None):
+        st = torch.cuda.current_stream().cuda_stream
+        if use_scratch:
+            s = lib.ckl_forward_noalloc(ctypes.byref(prob), H.data_ptr(), W.data_ptr(), idx.data_ptr(),
+                                        tl.data_ptr(), m.data_ptr(), loss.data_ptr(), lse.data_ptr(), rl.data_ptr(), st)
+        else:
+            s = lib.ckl_forward(ctypes.byref(prob), H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(),
+                                m.data_ptr(), loss.data_ptr(), lse.data_ptr(), rl.data_ptr(), ws.data_ptr(),
+                                ws.numel(), st)
+        B.check(s, lib)
+
+    def load(x):
+        h, w, i, t, mm = to_device(x)
+        for dst, src in ((H, h), (W, w), (idx, i), (tl, t), (m, mm)):
+            dst.copy_(src)
+
+    ws = torch.full((B.workspace_size(prob, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    refs = []
+    for x in xs:   # eager references (caller's workspace)
+        load(x)
+        call(False, ws)
+        torch.cuda.synchronize()
+        refs.append((loss.cpu().numpy().copy(), lse.cpu().numpy().copy(), rl.cpu().numpy().copy()))
+    say("case no-alloc forward captured in a graph")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # the scratch address is looked up on the first call, before capture
+        call(True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(True)
+    for rep in range(2):
+        for x, (l0, s0, r0) in zip(xs, refs):
+            load(x)                      # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(loss.cpu().numpy(), l0), rep
+            assert np.array_equal(lse.cpu().numpy(), s0), rep
+            assert np.array_equal(rl.cpu().numpy(), r0), rep
