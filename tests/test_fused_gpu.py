@@ -162,6 +162,65 @@ def test_fused_bitwise_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_fused_step_under_graph_capture():
+    # the one-call forward + backward (caller's workspace) captured in a HIP
+    # graph and replayed with new inputs copied into the captured buffers:
+    # every replay equals the eager call bit for bit
+    import ctypes
+
+    import torch
+
+    from chunked_kl_loss_amd import _binding as B
+    from tests.gpu_harness import to_device
+    lib = B.load_library()
+    xs = [inputs(4, T=2200, seed=s) for s in (21, 22)]
+    x0 = xs[0]
+    T, d, V, K = x0.T, x0.d, x0.V, x0.K
+    prob = B.make_problem(T, d, V, K, 512, B.CKL_BF16, B.CKL_F32, B.CKL_F32, compact_mask=True)
+    H, W, idx, tl, m = to_device(x0)
+    g = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lse = torch.zeros(T, dtype=torch.float32, device="cuda")
+    dH = torch.zeros((T, d), dtype=torch.float32, device="cuda")
+    dW = torch.zeros((V, d), dtype=torch.float32, device="cuda")
+    ws = torch.full((B.workspace_size(prob, 2),), 0xFF, dtype=torch.uint8, device="cuda")
+
+    def call():
+        B.check(lib.ckl_forward_backward(ctypes.byref(prob), H.data_ptr(), W.data_ptr(), idx.data_ptr(),
+                                         tl.data_ptr(), m.data_ptr(), g.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                                         None, dH.data_ptr(), dW.data_ptr(), ws.data_ptr(), ws.numel(),
+                                         torch.cuda.current_stream().cuda_stream), lib)
+
+    def load(x):
+        for dst, src in zip((H, W, idx, tl, m), to_device(x)):
+            dst.copy_(src)
+
+    refs = []
+    for x in xs:
+        load(x)
+        call()
+        torch.cuda.synchronize()
+        refs.append([t.cpu().numpy().copy() for t in (loss, lse, dH, dW)])
+    say("case one-call step captured in a graph")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(2):
+        for x, ref in zip(xs, refs):
+            load(x)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for t, r in zip((loss, lse, dH, dW), ref):
+                assert np.array_equal(t.cpu().numpy(), r), rep
+
+
 def test_fused_autograd_function():
     import torch
 
