@@ -267,7 +267,9 @@ def run(args) -> dict:
     prob = B.make_problem(T, d, V, K, chunk, in_code, in_code, B.CKL_F32, compact_mask=packed,
                           dw_group_rows=args.dw_group_rows)
     stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
+
+    def cur():  # the stream calls go to: the current one (a graph capture switches it)
+        return torch.cuda.current_stream(dev).cuda_stream
     P = ctypes.byref(prob)
     mp = None if mask is None else mask.data_ptr()
     peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
@@ -288,17 +290,17 @@ def run(args) -> dict:
 
         def fwd():
             B.check(lib.ckl_forward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
-                                    loss.data_ptr(), lse.data_ptr(), rl, ws_f.data_ptr(), ws_f.numel(), sp), lib)
+                                    loss.data_ptr(), lse.data_ptr(), rl, ws_f.data_ptr(), ws_f.numel(), cur()), lib)
 
         def bwd():
             B.check(lib.ckl_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
                                      lse.data_ptr(), None, dH.data_ptr(), dW.data_ptr(), ws_b.data_ptr(),
-                                     ws_b.numel(), sp), lib)
+                                     ws_b.numel(), cur()), lib)
 
         def both():
             B.check(lib.ckl_forward_backward(P, H.data_ptr(), W.data_ptr(), idx.data_ptr(), tl.data_ptr(), mp,
                                              None, loss.data_ptr(), lse.data_ptr(), rl, dH.data_ptr(),
-                                             dW.data_ptr(), ws_f.data_ptr(), ws_f.numel(), sp), lib)
+                                             dW.data_ptr(), ws_f.data_ptr(), ws_f.numel(), cur()), lib)
 
         if fused:
             fwd, bwd = both, (lambda: None)
@@ -324,6 +326,28 @@ def run(args) -> dict:
             fwd()
             bwd()
             torch.cuda.synchronize(dev)
+        run_f, run_b = fwd, bwd
+        if args.graph:
+            # the step captured in HIP graphs (forward and backward apart, so
+            # that the events still split them), replayed in the timed loop
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                fwd()
+                bwd()
+            stream.wait_stream(side)
+            torch.cuda.synchronize(dev)
+            graphs = []
+            for f in ((fwd,) if fused else (fwd, bwd)):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    f()
+                graphs.append(gr)
+            run_f = graphs[0].replay
+            run_b = (lambda: None) if fused else graphs[1].replay
+            run_f()
+            run_b()
+            torch.cuda.synchronize(dev)
         # timed steps: no per-kernel events
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -331,9 +355,9 @@ def run(args) -> dict:
         t_start = time.perf_counter()
         for i in range(steps):
             ev[i][0].record(stream)
-            fwd()
+            run_f()
             ev[i][1].record(stream)
-            bwd()
+            run_b()
             ev[i][2].record(stream)
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t_start
@@ -419,7 +443,7 @@ def run(args) -> dict:
                                                   if x.mask is not None else ")"),
         "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "chunk": chunk,
                    "masked_rows": T - n_kept, "packed_rows": packed, "parallelism": "single GPU",
-                   "path": args.path, "plan": plan},
+                   "path": args.path, "plan": plan, "graph": bool(args.graph)},
         "kept_tokens_per_s": n_kept / (step_ms * 1e-3),
         "tflops": flops_useful / (step_ms * 1e-3) / 1e12,
         "tflops_note": "8 N V d flops per step over the N unmasked rows, the method's count (forward, "
@@ -536,6 +560,8 @@ def main():
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="steps of the separate per-kernel timing pass (0 = skip; no roofline entry)")
     ap.add_argument("--no-compact", action="store_true", help="masked workloads: compute masked rows too")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of HIP graphs captured from them (torch.cuda.graph)")
     ap.add_argument("--dw-group-rows", type=int, default=0, help="one-call path: rows per dW update (0 = default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (for scaling HBM counters)")
