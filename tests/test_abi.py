@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from chunked_kl_loss_amd import _binding as B
@@ -269,3 +270,33 @@ def test_noalloc_forward_refusals(lib):
     assert st == B.CKL_ERR_UNSUPPORTED
     # the headline forward fits
     assert B.workspace_size(B.make_problem(32768, 2880, 201088, 100, 2048), 0) <= 64 << 20
+
+
+def test_plans_stay_inside_their_buffers(lib):
+    # host-side plan invariants over drawn problems, both dtypes: the dH split
+    # parts of the one-call path tile the padded vocabulary without reaching
+    # past it (a part wider than the padding would read unwritten row padding
+    # of G and W^T), chunks tile the padded rows, dW groups hold whole chunks,
+    # and the backward's G blocks tile the padded rows and vocabulary
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        bf16 = bool(rng.random() < 0.5)
+        tile_v, tile_t = (256, 256) if bf16 else (128, 128)
+        T = int(rng.integers(1, 300000))
+        V = int(rng.integers(1, 300000))
+        d = 8 * int(rng.integers(1, 600))
+        K = int(rng.integers(1, min(V, 4096) + 1))
+        chunk = int(rng.integers(1, 20000))
+        code = B.CKL_BF16 if bf16 else B.CKL_F32
+        prob = B.make_problem(T, d, V, K, chunk, code, dw_group_rows=int(rng.choice([0, 1, 5000, 10 ** 6])))
+        vp = -(-V // tile_v) * tile_v
+        tp = -(-T // tile_t) * tile_t
+        f = B.fused_plan(prob)
+        assert f["part_cols"] <= vp and f["part_cols"] % 8 == 0
+        assert (f["dh_parts"] - 1) * f["part_cols"] < vp <= f["dh_parts"] * f["part_cols"]
+        assert f["rows"] % 256 == 0 and (f["chunks"] - 1) * f["rows"] < tp <= f["chunks"] * f["rows"]
+        assert 1 <= f["dw_group_chunks"] <= f["chunks"]
+        b = B.backward_plan(prob)
+        assert b["Tc"] % tile_t == 0 and b["Vc"] % tile_v == 0
+        assert (b["nT"] - 1) * b["Tc"] < tp <= b["nT"] * b["Tc"]
+        assert (b["nV"] - 1) * b["Vc"] < vp <= b["nV"] * b["Vc"]
