@@ -365,7 +365,7 @@ def run(args) -> dict:
         bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
         step_ms = wall * 1e3 / steps
         peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
-        # what the driver sees in use (hipMemGetInfo): inputs, outputs, the
+        # what the runtime reports in use (hipMemGetInfo): inputs, outputs, the
         # workspaces as torch's allocator holds them, the library's code and
         # its static device array, against the free memory before the inputs
         used_gib = (free0 - torch.cuda.mem_get_info(dev)[0]) / 2**30
@@ -572,7 +572,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the loss shards by rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     peak = mfma_peak() if args.mfma_peak and not args.matrix else None  # before this process touches the GPU

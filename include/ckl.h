@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   CKL_OK = 0,
   CKL_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad alignment          */
-  CKL_ERR_UNSUPPORTED = 2, /* valid request outside what this build handles  */
+  CKL_ERR_UNSUPPORTED = 2, /* valid request outside what the library handles */
   CKL_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes below ckl_workspace_size()  */
   CKL_ERR_BAD_INDEX = 4,   /* validate = 1 found idx out of [0, V) or repeated */
   CKL_ERR_HIP = 5          /* a HIP runtime call failed                      */
