@@ -173,7 +173,16 @@ def test_fused_step_under_graph_capture():
     from chunked_kl_loss_amd import _binding as B
     from tests.gpu_harness import to_device
     lib = B.load_library()
-    xs = [inputs(4, T=2200, seed=s) for s in (21, 22)]
+    xs = []
+    for s in (21, 22):   # packed documents of 64..511 rows, the first quarter of each masked
+        rng = np.random.default_rng(s)
+        mask = np.ones(2200, np.uint8)
+        t = 0
+        while t < 2200:
+            n = int(rng.integers(64, 512))
+            mask[t:t + n // 4] = 0
+            t += n
+        xs.append(dataclasses.replace(_custom(2200, 256, 30000, 100, seed=s), mask=mask))
     x0 = xs[0]
     T, d, V, K = x0.T, x0.d, x0.V, x0.K
     prob = B.make_problem(T, d, V, K, 512, B.CKL_BF16, B.CKL_F32, B.CKL_F32, compact_mask=True)

@@ -97,8 +97,20 @@ def test_noalloc_forward_under_graph_capture():
     # (torch.cuda.graph) and replayed with new inputs copied into the captured
     # buffers, eager work and synchronisation between replays; every replay
     # equals an eager ckl_forward on the same inputs, bit for bit
+    import dataclasses
+
+    from tests.test_parity_gpu import _custom
     lib = B.load_library()
-    xs = [make_inputs(4, seed=s, T=3000) for s in (7, 8, 9)]   # packed-document masks
+    xs = []
+    for s in (7, 8, 9):   # packed documents of 64..511 rows, the first quarter of each masked
+        rng = np.random.default_rng(s)
+        mask = np.ones(3000, np.uint8)
+        t = 0
+        while t < 3000:
+            n = int(rng.integers(64, 512))
+            mask[t:t + n // 4] = 0
+            t += n
+        xs.append(dataclasses.replace(_custom(3000, 256, 30000, 100, "bf16", seed=s), mask=mask))
     x0 = xs[0]
     T, d, V, K = x0.T, x0.d, x0.V, x0.K
     prob = B.make_problem(T, d, V, K, 256, B.CKL_BF16, compact_mask=True)
