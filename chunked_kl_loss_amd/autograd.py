@@ -40,7 +40,8 @@ class ChunkedKLLoss(torch.autograd.Function):
 
 class FusedChunkedKLLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048, teacher_form: int = 0):
+    def forward(ctx, H, W, idx, tlogit, mask=None, chunk: int = 2048, teacher_form: int = 0,
+                dw_group_rows: int = 0):
         need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         ctx.dtypes = (H.dtype, W.dtype)
         if not (need_h or need_w):
@@ -51,7 +52,7 @@ class FusedChunkedKLLoss(torch.autograd.Function):
         # gradient is known
         loss, _, _, dH, dW = _binding.forward_backward(H, W, idx, tlogit, mask, None, chunk=chunk,
                                                        dh_dtype=torch.float32, dw_dtype=torch.float32,
-                                                       teacher_form=teacher_form)
+                                                       teacher_form=teacher_form, dw_group_rows=dw_group_rows)
         ctx.save_for_backward(dH if need_h else torch.empty(0, device=H.device),
                               dW if need_w else torch.empty(0, device=H.device))
         return loss[0]
@@ -66,15 +67,18 @@ class FusedChunkedKLLoss(torch.autograd.Function):
             dH = _binding.scale_cast(dH32, torch.empty(dH32.shape, dtype=h_dtype, device=dH32.device), g)
         if ctx.needs_input_grad[1]:
             dW = _binding.scale_cast(dW32, torch.empty(dW32.shape, dtype=w_dtype, device=dW32.device), g)
-        return dH, dW, None, None, None, None, None
+        return dH, dW, None, None, None, None, None, None
 
 
-def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False, teacher_form: int = 0):
+def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool = False, teacher_form: int = 0,
+                    dw_group_rows: int = 0):
     """Mean forward KL(teacher || student) over unmasked rows, differentiable
     with respect to H and W.  fused=True computes the gradients together with
-    the loss (one pass over the logits, chunk x V extra workspace).
+    the loss (one pass over the logits; it keeps the logit gradients of up to
+    dw_group_rows rows, 0 = the library default of min(16384, 8 chunks), so
+    a smaller value holds less memory and updates dW more often).
     teacher_form 1: tlogit holds truncated teacher log-probabilities, used as
     given (teacher mass below one)."""
     if fused:
-        return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)
+        return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form, dw_group_rows)
     return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)

@@ -246,6 +246,12 @@ def test_fused_autograd_function():
     assert H.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
     assert max_rel(H.grad.double().cpu().numpy(), ref["dH"]) <= 1e-2
     assert max_rel(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-2
+    # one chunk per dW update: the same gradients up to the fp32 grouping of dW
+    H2 = H.detach().clone().requires_grad_(True)
+    W2 = W.detach().clone().requires_grad_(True)
+    (2.0 * ckl.chunked_kl_loss(H2, W2, idx, tl, m, chunk=256, fused=True, dw_group_rows=256)).backward()
+    assert torch.equal(H2.grad, H.grad)
+    assert max_rel(W2.grad.double().cpu().numpy(), W.grad.double().cpu().numpy()) <= 2 ** -7
 
 
 def test_fused_logprob_teacher():
