@@ -232,6 +232,18 @@ def _check_inputs(H, W, idx, tlogit, mask):
     if mask is not None:
         if mask.shape != (H.shape[0],) or mask.dtype not in (torch.uint8, torch.bool) or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous uint8/bool [T] tensor")
+        if not mask.is_cuda:
+            raise ValueError("mask must be a GPU tensor")
+    devs = {t.device for t in (H, W, idx, tlogit) + ((mask,) if mask is not None else ())}
+    if len(devs) != 1:
+        raise ValueError("H, W, idx, tlogit and mask must be on one device")
+
+
+def _check_lse(lse, H):
+    torch = _torch()
+    if (not lse.is_cuda or lse.device != H.device or lse.dtype != torch.float32 or lse.shape != (H.shape[0],)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [T] tensor on the device of H")
 
 
 def _stream_ptr(device):
@@ -269,6 +281,7 @@ def backward(H, W, idx, tlogit, mask, lse, grad_loss=None, chunk: int = 2048, dh
     """Returns (dH, dW) of grad_loss * loss (grad_loss: [1] float32 tensor or None = 1)."""
     torch = _torch()
     _check_inputs(H, W, idx, tlogit, mask)
+    _check_lse(lse, H)
     T, d = H.shape
     V, K = W.shape[0], idx.shape[1]
     in_code = _dtype_code(H.dtype)
@@ -351,8 +364,15 @@ def shard_combine(lse_parts, cross_parts, idx, tlogit, mask=None, v_total: int =
     n_shards, T = lse_parts.shape
     K = idx.shape[1]
     for name, t in (("lse_parts", lse_parts), ("cross_parts", cross_parts), ("idx", idx), ("tlogit", tlogit)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if not t.is_cuda or not t.is_contiguous() or t.device != lse_parts.device:
+            raise ValueError(f"{name} must be a contiguous GPU tensor on the device of lse_parts")
+    if (cross_parts.shape != lse_parts.shape or lse_parts.dtype != torch.float32 or cross_parts.dtype != torch.float32
+            or idx.shape != tlogit.shape or idx.shape[0] != T or idx.dtype != torch.int32
+            or tlogit.dtype != torch.float32):
+        raise ValueError("lse_parts, cross_parts: float32 [n_shards, T]; idx int32 and tlogit float32 [T, K]")
+    if mask is not None and (mask.shape != (T,) or mask.dtype not in (torch.uint8, torch.bool) or not mask.is_cuda
+                             or not mask.is_contiguous() or mask.device != lse_parts.device):
+        raise ValueError("mask must be a contiguous uint8/bool [T] tensor on the device of lse_parts")
     prob = make_problem(T, d, v_total, K, 1, CKL_F32, teacher_form=teacher_form)
     lib = load_library()
     ws_bytes = workspace_size(prob, 3)

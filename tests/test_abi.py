@@ -300,3 +300,22 @@ def test_plans_stay_inside_their_buffers(lib):
         assert b["Tc"] % tile_t == 0 and b["Vc"] % tile_v == 0
         assert (b["nT"] - 1) * b["Tc"] < tp <= b["nT"] * b["Tc"]
         assert (b["nV"] - 1) * b["Vc"] < vp <= b["nV"] * b["Vc"]
+
+
+def test_binding_refuses_host_tensors():
+    # the binding hands only device pointers to the library: host tensors are refused before any call
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    H = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(6, 8, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    tl = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        ckl.forward(H, W, idx, tl)
+    with pytest.raises(ValueError):
+        ckl.forward_backward(H, W, idx, tl)
+    with pytest.raises(ValueError):
+        ckl.backward(H, W, idx, tl, None, torch.zeros(4))
+    with pytest.raises(ValueError):
+        ckl.shard_combine(torch.zeros(2, 4), torch.zeros(2, 4), idx, tl, v_total=6, d=8)

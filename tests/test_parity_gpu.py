@@ -227,6 +227,27 @@ def test_side_stream_matches_default_stream():
             assert np.array_equal(r[k], q[k]), k
 
 
+def test_binding_rejects_misplaced_tensors():
+    # host tensors or mismatched arguments are refused before any launch
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    from tests.gpu_harness import to_device
+    x = _custom(64, 32, 500, 5)
+    H, W, idx, tl, _ = to_device(x)
+    with pytest.raises(ValueError):
+        ckl.forward(H, W, idx, tl, torch.ones(64, dtype=torch.uint8))          # mask on the host
+    with pytest.raises(ValueError):
+        ckl.forward(H.cpu(), W, idx, tl)
+    loss, lse, _ = ckl.forward(H, W, idx, tl)
+    with pytest.raises(ValueError):
+        ckl.backward(H, W, idx, tl, None, lse.cpu())                             # lse on the host
+    with pytest.raises(ValueError):
+        ckl.backward(H, W, idx, tl, None, lse[:10])                              # lse of another size
+    with pytest.raises(ValueError):
+        ckl.backward(H, W, idx, tl, None, lse.double())
+
+
 def test_autograd_function():
     import torch
 
