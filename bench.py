@@ -348,6 +348,14 @@ def run(args) -> dict:
             run_f()
             run_b()
             torch.cuda.synchronize(dev)
+        if args.min_time > 0:
+            # short steps: enough of them to fill min_time seconds
+            torch.cuda.synchronize(dev)
+            t1 = time.perf_counter()
+            run_f()
+            run_b()
+            torch.cuda.synchronize(dev)
+            steps = max(steps, int(np.ceil(args.min_time / max(time.perf_counter() - t1, 1e-6))))
         # timed steps: no per-kernel events
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -383,7 +391,7 @@ def run(args) -> dict:
         del ws_f, ws_b, dH, dW, loss, lse, row_loss
         torch.cuda.empty_cache()
         return dict(path=path, plan=plan, step_ms=step_ms, peak_gib=peak_gib, used_gib=used_gib, kt=kt,
-                    parity=parity,
+                    parity=parity, steps=steps,
                     fwd_ms=None if fused else float(np.mean(fwd_ms)),
                     bwd_ms=None if fused else float(np.mean(bwd_ms)),
                     fwd_ms_min=None if fused else float(np.min(fwd_ms)),
@@ -431,7 +439,7 @@ def run(args) -> dict:
         "value": T / (step_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": m["steps"],
         "warmup": args.warmup,
         "ms_per_step": step_ms,
         "higher_is_better": True,
@@ -508,7 +516,7 @@ def matrix(args) -> dict:
         for path in ("fused", "recompute"):
             cmd = [sys.executable, os.path.abspath(__file__), "--workload", str(wl), "--path", path,
                    "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-compare",
-                   "--cpu-rows", "0", "--kernel-steps", "0"]
+                   "--cpu-rows", "0", "--kernel-steps", "0", "--min-time", str(args.min_time or 1.0)]
             if chunk:
                 cmd += ["--chunk", str(chunk)]
             name = f"workload {wl} chunk {chunk or WORKLOADS[wl].chunk} path {path}"
@@ -535,7 +543,7 @@ def matrix(args) -> dict:
                          "hbm_in_use_gib_mem_get_info": row["hbm_in_use_gib_mem_get_info"],
                          "fwd_ms": row["fwd_ms"], "bwd_ms": row["bwd_ms"], "fwd_ms_min": row["fwd_ms_min"],
                          "bwd_ms_min": row["bwd_ms_min"], "step_ms_events_min": row["step_ms_events_min"],
-                         "parity": row["parity"], "wall_s": time.perf_counter() - t0})
+                         "parity": row["parity"], "steps": row["steps"], "wall_s": time.perf_counter() - t0})
             log(f"  {row['ms_per_step']:.1f} ms/step, peak {row['peak_hbm_gib']:.2f} GiB, "
                 f"parity {'pass' if row['parity'] and row['parity']['pass'] else 'FAIL'}")
     return {"metric": METRIC, "matrix": rows, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -569,6 +577,9 @@ def main():
     ap.add_argument("--mfma-peak", action=argparse.BooleanOptionalAction, default=True,
                     help="measure the sustained bf16 MFMA rate with a microbenchmark (hipcc, child process)")
     ap.add_argument("--case-timeout", type=int, default=300, help="--matrix: seconds per case")
+    ap.add_argument("--min-time", type=float, default=0.0,
+                    help="time at least this many seconds of steps (more than --steps where steps are short; "
+                         "0 = exactly --steps; --matrix cases default to 1)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
