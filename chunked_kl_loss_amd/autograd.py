@@ -78,7 +78,17 @@ def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool
     dw_group_rows rows, 0 = the library default of min(16384, 8 chunks), so
     a smaller value holds less memory and updates dW more often).
     teacher_form 1: tlogit holds truncated teacher log-probabilities, used as
-    given (teacher mass below one)."""
+    given (teacher mass below one).
+
+    The library takes contiguous tensors, int32 indices and fp32 teacher
+    values: other layouts and integer / float types are converted here (no
+    copy when they already match; H and W keep their dtype, which selects the
+    bf16 or fp32 path)."""
+    H, W = H.contiguous(), W.contiguous()
+    idx = idx.to(torch.int32).contiguous()
+    tlogit = tlogit.to(torch.float32).contiguous()
+    if mask is not None:
+        mask = mask.contiguous()
     if fused:
         return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form, dw_group_rows)
     return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)

@@ -266,6 +266,31 @@ def test_autograd_function():
     assert max_rel(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-2
 
 
+def test_autograd_converts_layouts_and_index_types():
+    # a strided view of H, int64 indices and bf16 teacher values give the
+    # result of the contiguous int32 / fp32 call, and the gradient reaches
+    # the tensor the view was taken from
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    from tests.gpu_harness import to_device
+    x = _custom(300, 64, 5000, 20)
+    H, W, idx, tl, _ = to_device(x)
+    tl = tl.to(torch.bfloat16).float()  # values that bf16 holds exactly
+    for fused in (False, True):
+        ref_H = H.clone().requires_grad_(True)
+        ref = ckl.chunked_kl_loss(ref_H, W, idx, tl, chunk=128, fused=fused)
+        ref.backward()
+        wide = torch.zeros(x.T, 2 * x.d, dtype=H.dtype, device=H.device)
+        wide[:, ::2] = H
+        wide.requires_grad_(True)
+        got = ckl.chunked_kl_loss(wide[:, ::2], W, idx.long(), tl.to(torch.bfloat16), chunk=128, fused=fused)
+        got.backward()
+        assert got.item() == ref.item()
+        assert torch.equal(wide.grad[:, ::2], ref_H.grad)
+        assert not wide.grad[:, 1::2].any()
+
+
 # ------------------------------------------- teacher given as log-probs ----
 def test_logprob_teacher_fp32_full():
     x = with_logprob_teacher(inputs(0), n_neg_inf=5)
