@@ -80,15 +80,19 @@ def chunked_kl_loss(H, W, idx, tlogit, mask=None, chunk: int = 2048, fused: bool
     teacher_form 1: tlogit holds truncated teacher log-probabilities, used as
     given (teacher mass below one).
 
-    The library takes contiguous tensors, int32 indices and fp32 teacher
-    values: other layouts and integer / float types are converted here (no
-    copy when they already match; H and W keep their dtype, which selects the
-    bf16 or fp32 path)."""
-    H, W = H.contiguous(), W.contiguous()
-    idx = idx.to(torch.int32).contiguous()
-    tlogit = tlogit.to(torch.float32).contiguous()
+    Leading batch dimensions are flattened into rows: H [..., d], idx and
+    tlogit [..., K], mask [...].  The library takes contiguous tensors, int32
+    indices and fp32 teacher values: other layouts and integer / float types
+    are converted here (no copy when they already match; H and W keep their
+    dtype, which selects the bf16 or fp32 path)."""
+    d, K = H.shape[-1], idx.shape[-1]
+    if idx.shape[:-1] != H.shape[:-1] or tlogit.shape != idx.shape or (mask is not None and mask.shape != H.shape[:-1]):
+        raise ValueError("H [..., d], idx and tlogit [..., K] and mask [...] must share their leading dimensions")
+    H, W = H.reshape(-1, d).contiguous(), W.contiguous()
+    idx = idx.reshape(-1, K).to(torch.int32).contiguous()
+    tlogit = tlogit.reshape(-1, K).to(torch.float32).contiguous()
     if mask is not None:
-        mask = mask.contiguous()
+        mask = mask.reshape(-1).contiguous()
     if fused:
         return FusedChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form, dw_group_rows)
     return ChunkedKLLoss.apply(H, W, idx, tlogit, mask, chunk, teacher_form)

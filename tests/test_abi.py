@@ -319,3 +319,18 @@ def test_binding_refuses_host_tensors():
         ckl.backward(H, W, idx, tl, None, torch.zeros(4))
     with pytest.raises(ValueError):
         ckl.shard_combine(torch.zeros(2, 4), torch.zeros(2, 4), idx, tl, v_total=6, d=8)
+
+
+def test_loss_function_refuses_mismatched_batch_shapes():
+    # leading dimensions of H, idx, tlogit and mask must agree: refused before any call
+    import torch
+
+    import chunked_kl_loss_amd as ckl
+    H, W = torch.zeros(2, 3, 8), torch.zeros(5, 8)
+    with pytest.raises(ValueError):
+        ckl.chunked_kl_loss(H, W, torch.zeros(2, 4, 2, dtype=torch.int32), torch.zeros(2, 4, 2))
+    with pytest.raises(ValueError):
+        ckl.chunked_kl_loss(H, W, torch.zeros(2, 3, 2, dtype=torch.int32), torch.zeros(2, 3, 3))
+    with pytest.raises(ValueError):
+        ckl.chunked_kl_loss(H, W, torch.zeros(2, 3, 2, dtype=torch.int32), torch.zeros(2, 3, 2),
+                            torch.ones(6, dtype=torch.uint8))

@@ -289,6 +289,18 @@ def test_autograd_converts_layouts_and_index_types():
         assert got.item() == ref.item()
         assert torch.equal(wide.grad[:, ::2], ref_H.grad)
         assert not wide.grad[:, 1::2].any()
+    # batch dimensions: [2, 150, d] hidden states with a [2, 150] mask
+    mask = torch.from_numpy((np.random.default_rng(3).random(x.T) < 0.7).astype(np.uint8)).to(H.device)
+    for fused in (False, True):
+        ref_H = H.clone().requires_grad_(True)
+        ref = ckl.chunked_kl_loss(ref_H, W, idx, tl, mask, chunk=128, fused=fused)
+        ref.backward()
+        Hb = H.reshape(2, x.T // 2, x.d).clone().requires_grad_(True)
+        got = ckl.chunked_kl_loss(Hb, W, idx.reshape(2, x.T // 2, -1), tl.reshape(2, x.T // 2, -1),
+                                  mask.reshape(2, x.T // 2), chunk=128, fused=fused)
+        got.backward()
+        assert got.item() == ref.item()
+        assert torch.equal(Hb.grad.reshape(x.T, x.d), ref_H.grad)
 
 
 # ------------------------------------------- teacher given as log-probs ----
