@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -436,6 +437,30 @@ hipError_t pack_rows(const Plan& q, const Packed& k, const uint8_t* mask, const 
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// A buffer of an entry point: where it starts, its bytes, its name.
+struct Span {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+// Every buffer the call writes (outputs, the used part of the workspace) must
+// be disjoint from every other buffer of the call: an output that aliases an
+// input or the workspace would be read after the library overwrote it.
+ckl_status check_disjoint(std::initializer_list<Span> written, std::initializer_list<Span> read) {
+  for (auto w = written.begin(); w != written.end(); ++w) {
+    for (auto o = w + 1; o != written.end(); ++o)
+      if (overlap(*w, *o)) return fail(CKL_ERR_INVALID_ARG, "%s and %s overlap", w->name, o->name);
+    for (const Span& r : read)
+      if (overlap(*w, r)) return fail(CKL_ERR_INVALID_ARG, "%s overlaps %s", w->name, r.name);
+  }
+  return CKL_OK;
+}
+
 // ------------------------------------------------ allocation-free forward --
 // ckl_forward_noalloc takes its workspace from this file-scope device array
 // instead of a caller's buffer.  Every device the library runs on holds its
@@ -507,6 +532,13 @@ ckl_status ckl_forward(const ckl_problem* p, const void* H, const void* W, const
   const FwdWs w = fwd_layout(q, p);
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", w.total, ws ? ws_bytes : (size_t)0);
+  {
+    const size_t T = q.T, K = q.K;
+    s = check_disjoint({{loss, 4, "loss"}, {lse, T * 4, "lse"}, {row_loss, T * 4, "row_loss"}, {ws, w.total, "ws"}},
+                       {{H, T * q.d * q.esz, "H"}, {W, (size_t)q.V * q.d * q.esz, "W"}, {idx, T * K * 4, "idx"},
+                        {tlogit, T * K * 4, "tlogit"}, {mask, T, "mask"}});
+    if (s != CKL_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   char* b = (char*)ws;
   int* idx_s = (int*)(b + w.idx_s);
@@ -628,6 +660,15 @@ ckl_status ckl_backward(const ckl_problem* p, const void* H, const void* W, cons
   const BwdWs w = bwd_layout(q, p);
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", w.total, ws ? ws_bytes : (size_t)0);
+  {
+    const size_t T = q.T, K = q.K, d = q.d;
+    s = check_disjoint({{dH, T * d * (p->dh_dtype == CKL_BF16 ? 2 : 4), "dH"},
+                        {dW, (size_t)q.V * d * (p->dw_dtype == CKL_BF16 ? 2 : 4), "dW"}, {ws, w.total, "ws"}},
+                       {{H, T * d * q.esz, "H"}, {W, (size_t)q.V * d * q.esz, "W"}, {idx, T * K * 4, "idx"},
+                        {tlogit, T * K * 4, "tlogit"}, {mask, T, "mask"}, {lse, T * 4, "lse"},
+                        {grad_loss, 4, "grad_loss"}});
+    if (s != CKL_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   char* b = (char*)ws;
   int* idx_s = (int*)(b + w.idx_s);
@@ -760,6 +801,15 @@ ckl_status ckl_forward_backward(const ckl_problem* p, const void* H, const void*
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "forward + backward workspace needs %zu bytes, got %zu", w.total,
                 ws ? ws_bytes : (size_t)0);
+  {
+    const size_t T = q.T, K = q.K, d = q.d;
+    s = check_disjoint({{loss, 4, "loss"}, {lse, T * 4, "lse"}, {row_loss, T * 4, "row_loss"},
+                        {dH, T * d * (p->dh_dtype == CKL_BF16 ? 2 : 4), "dH"},
+                        {dW, (size_t)q.V * d * (p->dw_dtype == CKL_BF16 ? 2 : 4), "dW"}, {ws, w.total, "ws"}},
+                       {{H, T * d * q.esz, "H"}, {W, (size_t)q.V * d * q.esz, "W"}, {idx, T * K * 4, "idx"},
+                        {tlogit, T * K * 4, "tlogit"}, {mask, T, "mask"}, {grad_loss, 4, "grad_loss"}});
+    if (s != CKL_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   char* b = (char*)ws;
   int* idx_s = (int*)(b + w.idx_s);
@@ -930,6 +980,13 @@ ckl_status ckl_shard_forward(const ckl_problem* p, const void* H, const void* W,
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "shard forward workspace needs %zu bytes, got %zu", w.total,
                 ws ? ws_bytes : (size_t)0);
+  {
+    const size_t T = q.T, K = q.K;
+    s = check_disjoint({{lse_part, T * 4, "lse_part"}, {cross_part, T * 4, "cross_part"}, {ws, w.total, "ws"}},
+                       {{H, T * q.d * q.esz, "H"}, {W, (size_t)q.V * q.d * q.esz, "W"}, {idx, T * K * 4, "idx"},
+                        {tlogit, T * K * 4, "tlogit"}});
+    if (s != CKL_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   char* b = (char*)ws;
   int* idx_s = (int*)(b + w.idx_s);
@@ -990,6 +1047,13 @@ ckl_status ckl_shard_combine(const ckl_problem* p, int32_t n_shards, const float
   if (!ws || ws_bytes < w.total)
     return fail(CKL_ERR_WORKSPACE, "shard combine workspace needs %zu bytes, got %zu", w.total,
                 ws ? ws_bytes : (size_t)0);
+  {
+    const size_t T = q.T, K = q.K, parts = (size_t)n_shards * T * 4;
+    s = check_disjoint({{loss, 4, "loss"}, {lse, T * 4, "lse"}, {row_loss, T * 4, "row_loss"}, {ws, w.total, "ws"}},
+                       {{lse_parts, parts, "lse_parts"}, {cross_parts, parts, "cross_parts"}, {idx, T * K * 4, "idx"},
+                        {tlogit, T * K * 4, "tlogit"}, {mask, T, "mask"}});
+    if (s != CKL_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   char* b = (char*)ws;
   int* N = (int*)(b + w.N);

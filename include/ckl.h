@@ -50,7 +50,11 @@
  * workspace: there are no floating-point atomics.
  *
  * Errors.  Arguments are checked on the host before anything is enqueued;
- * on error nothing is launched and outputs are untouched.  HIP launch errors
+ * on error nothing is launched and outputs are untouched.  Every buffer a
+ * call writes (its outputs and the used part of its workspace) must be
+ * disjoint from every other buffer of the call, or the call returns
+ * CKL_ERR_INVALID_ARG (the check compares address ranges; it cannot see
+ * two mappings of one allocation).  HIP launch errors
  * return CKL_ERR_HIP.  ckl_last_error() returns a thread-local message that
  * describes the last non-OK status returned on the calling thread.
  */

@@ -334,3 +334,45 @@ def test_loss_function_refuses_mismatched_batch_shapes():
     with pytest.raises(ValueError):
         ckl.chunked_kl_loss(H, W, torch.zeros(2, 3, 2, dtype=torch.int32), torch.zeros(2, 3, 2),
                             torch.ones(6, dtype=torch.uint8))
+
+
+def test_aliased_buffers_rejected(lib):
+    # an output that overlaps an input, another output or the workspace is refused on the host
+    p = _prob()
+    need_f, need_b, need_fb = (B.workspace_size(p, w) for w in (0, 1, 2))
+    far = 1 << 34  # 16 GiB apart: larger than any buffer of this problem
+    H, W, idx, tl, mask, lse, loss, dH, dW, ws = ((1 << 40) + i * far for i in range(10))
+    P = ctypes.byref(p)
+
+    def err():
+        return lib.ckl_last_error().decode()
+
+    # forward: lse written over W, the workspace over the teacher values, loss inside lse
+    assert lib.ckl_forward(P, H, W, idx, tl, mask, loss, W + 256, None, ws, need_f, None) == B.CKL_ERR_INVALID_ARG
+    assert "lse overlaps W" in err()
+    assert lib.ckl_forward(P, H, W, idx, tl, mask, loss, lse, None, tl - 64, need_f, None) == B.CKL_ERR_INVALID_ARG
+    assert "ws overlaps tlogit" in err()
+    assert lib.ckl_forward(P, H, W, idx, tl, mask, lse + 16, lse, None, ws, need_f, None) == B.CKL_ERR_INVALID_ARG
+    assert "overlap" in err()
+    # backward: dH in place of H, dW over the LSE input
+    assert lib.ckl_backward(P, H, W, idx, tl, mask, lse, None, H, dW, ws, need_b, None) == B.CKL_ERR_INVALID_ARG
+    assert "dH overlaps H" in err()
+    assert lib.ckl_backward(P, H, W, idx, tl, mask, lse, None, dH, lse, ws, need_b, None) == B.CKL_ERR_INVALID_ARG
+    assert "dW overlaps lse" in err()
+    # one call: dH and dW sharing memory, the workspace over the mask
+    assert lib.ckl_forward_backward(P, H, W, idx, tl, mask, None, loss, lse, None, dH, dH + 16, ws, need_fb,
+                                    None) == B.CKL_ERR_INVALID_ARG
+    assert "dH and dW overlap" in err()
+    assert lib.ckl_forward_backward(P, H, W, idx, tl, mask, None, loss, lse, None, dH, dW, mask, need_fb,
+                                    None) == B.CKL_ERR_INVALID_ARG
+    assert "ws overlaps mask" in err()
+    # shards: a partial written over the hidden states; the combined LSE over the partials
+    shard = _prob(V=1000, v_offset=1000, v_total=2048)
+    need_s = B.workspace_size(shard, 0)
+    assert lib.ckl_shard_forward(ctypes.byref(shard), H, W, idx, tl, H + 32, lse, ws, need_s,
+                                 None) == B.CKL_ERR_INVALID_ARG
+    assert "lse_part overlaps H" in err()
+    need_c = B.workspace_size(shard, 3)
+    assert lib.ckl_shard_combine(ctypes.byref(shard), 2, dH, dW, idx, tl, None, loss, dH + 16, None, ws, need_c,
+                                 None) == B.CKL_ERR_INVALID_ARG
+    assert "lse overlaps lse_parts" in err()
