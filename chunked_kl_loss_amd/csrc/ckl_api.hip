@@ -64,7 +64,7 @@ constexpr int64_t kDwChunks = 8;
 // stride of 32 KiB + 256 bytes made the G formation ~1.2x slower than
 // 32 KiB + 640 bytes).
 constexpr int64_t kGtPad = 320;
-// The backward keeps one G block, stored as G and G^T, within chunk * V
+// The backward keeps one G block (fp32: and its transpose) within chunk * V
 // elements.  (Double-buffering it to overlap the recompute of block i+1 with
 // the contraction of block i on a second stream measured no faster: both
 // kernels are throughput-bound, so concurrency only splits the CUs.)
@@ -212,8 +212,10 @@ Plan make_plan(const ckl_problem* p) {
   q.Tp = round_up(q.T, q.BN);
   q.Vp = round_up(q.V, q.BM);
 
-  // G blocks of Tc token rows x Vc vocabulary columns, both stored twice (G and
-  // G^T), within chunk * V elements in total.  Among the admissible shapes pick
+  // G blocks of Tc token rows x Vc vocabulary columns, within chunk * V
+  // elements for G and G^T together (bf16 keeps G alone and still takes half
+  // the budget: a G block of the whole budget measured slower at 32K rows,
+  // faster at 131K).  Among the admissible shapes pick
   // the one with the least fp32 read-modify-write of dH (once per extra
   // vocabulary block) and dW (once per extra token block).
   const int64_t per_layout = std::max<int64_t>(p->chunk * p->V / (2 * kGBuffers), q.BM * q.BN);
@@ -367,8 +369,8 @@ FusedWs fused_layout(const Plan& q, const ckl_problem* p) {
   // H^T of one dW group's rows at a time (its update reads no other rows)
   w.Ht = take((size_t)q.d * (q.Gc * q.Cs + kLdPad) * q.esz);
   w.Wt = take((size_t)q.d * (q.Vp + kLdPad) * q.esz);
-  // bf16: u of a chunk in the forward's tile order, laid out as G and G^T
-  // by gpass_tiles (fp32 keeps u in G itself)
+  // bf16: u of a chunk in the forward's tile order, laid out as G by
+  // gpass_tiles (fp32 keeps u in G itself)
   w.U = q.in_bf16 ? take((size_t)q.Cs * q.Vp * q.esz) : 0;
   // bf16: G of the group's chunks, read k-major by the dW update (no G^T);
   // fp32: G of one chunk and G^T of the group's chunks

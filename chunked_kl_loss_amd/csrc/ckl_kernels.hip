@@ -14,8 +14,15 @@
 // apply the closed-form gradient):
 //   bwd_grad       recompute the logit tiles of one G block and turn them into
 //                  G = s (M 2^{z log2 e - LSE log2 e} - p~), rounded once to
-//                  the input dtype, stored as G and G^T
+//                  the input dtype, stored as G (fp32: also as G^T)
 //   gemm_store     dH (+)= G W and dW (+)= G^T H on the same MFMA main loop
+//                  (bf16 reads G itself k-major for dW)
+// One call without recompute (forward and backward together, per row chunk):
+//   fwd_lse<STORE> as fwd_lse, keeping u = 2^{z log2 e - m} of every tile
+//   gpass_tiles    once the chunk's LSE is known, u -> G (gpass_kernel: fp32)
+//   gfix           the teacher columns of G, from the gathered logits
+//   gemm_store     dH of the chunk as split-k parts, dW once per group of chunks
+//   splitk_sum     the parts summed in a fixed order
 #include "ckl_kernels.hpp"
 
 #include <type_traits>
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(C::NTHREADS) void fwd_lse_kernel(
   // contribute partial maxima, sums and gathered logits for the tile.
   static_assert(NBK == L::GROUPS && GLANES == BLK, "one column block per lane group");
   // bf16 keeps u in tile order (whole 1 KiB stores; gpass_tiles_kernel lays
-  // it out as G and G^T), fp32 at G[t][v] directly
+  // it out as G), fp32 at G[t][v] directly
   constexpr bool kTileU = sizeof(TIn) == 2;
   static_assert(!kTileU || (RPB == 16 && C::BM == 256 && C::BN == 256), "tile order of the bf16 configuration");
   // Between tiles the entry after the owner's next teacher index waits in

@@ -5,12 +5,15 @@
 //   logits      z^T[v, t] = sum_j W[v, j]  H[t, j]      (X = W,   Y = H)
 //   dH          dH[t, j]  = sum_v G[t, v]  W^T[j, v]    (X = G,   Y = W^T)
 //   dW          dW[v, j]  = sum_t G^T[v, t] H^T[j, t]   (X = G^T, Y = H^T)
-// so one main loop serves all of them and only the epilogues differ.
+// so one main loop serves all of them and only the epilogues differ; the bf16
+// loop also takes X k-major (dW reads G itself, no G^T is formed).
 //
 // A workgroup owns a BM x BN output tile split over a WAVES_M x WAVES_N grid
 // of 64-wide wavefronts; each wave owns WM x WN = (MB x NB) blocks of the
-// 32x32 MFMA.  K is walked in BK slices staged through two LDS buffers; the
-// next slice is fetched into registers while the current one is multiplied.
+// 32x32 MFMA.  K is walked in BK slices staged through two LDS buffers: the
+// bf16 loop loads them global->LDS directly (buffer_load ... lds), the fp32
+// loop fetches the next slice into registers while the current one is
+// multiplied.
 #pragma once
 
 #include <type_traits>
