@@ -504,13 +504,14 @@ def run(args) -> dict:
     return result
 
 
-def matrix(args) -> dict:
-    """Workloads 1-4 and the packed-document chunk sweep, each (workload,
-    chunk, path) in its own child process (started before this process
-    touches the GPU); a child that fails or runs out of memory gives a FAILED
-    row and the sweep goes on."""
+def matrix(args, cases=None) -> dict:
+    """Workloads 1-4 and the packed-document chunk sweep (or the given
+    (workload, chunk or None) cases), each (workload, chunk, path) in its own
+    child process (started before this process touches the GPU); a child that
+    fails or runs out of memory gives a FAILED row and the sweep goes on."""
     from synth import WORKLOADS
-    cases = [(1, None), (2, None), (3, None)] + [(4, c) for c in WORKLOADS[4].chunk_sweep]
+    if cases is None:
+        cases = [(1, None), (2, None), (3, None)] + [(4, c) for c in WORKLOADS[4].chunk_sweep]
     rows = []
     for wl, chunk in cases:
         for path in ("fused", "recompute"):

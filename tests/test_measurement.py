@@ -112,3 +112,22 @@ def test_bench_parity_check_passes_exact_and_catches_errors():
             row = (r["vocab_rows"] if key == "dW" else r["rows"])[-1]
             bad[key][row, 0] += 1e-3 * np.abs(bad[key]).max()
         assert not bench.parity_sample(x, bad)["pass"], key
+
+
+def test_matrix_records_failed_cases_and_goes_on():
+    # each case runs in a child process; here (no GPU) every child fails, and
+    # each failure becomes a FAILED row with its error while the sweep goes on
+    import argparse
+    import torch
+
+    import bench
+    if torch.cuda.is_available():
+        pytest.skip("needs a machine without a GPU: the children must fail")
+    args = argparse.Namespace(steps=1, warmup=0, min_time=0.0, case_timeout=120)
+    r = bench.matrix(args, cases=[(1, None), (4, 512)])
+    assert r["isolation"] == "one child process per (workload, chunk, path)"
+    rows = r["matrix"]
+    assert [(x["workload"], x["chunk"], x["path"]) for x in rows] == [
+        ("small-bf16", 1024, "fused"), ("small-bf16", 1024, "recompute"),
+        ("t256k-v201k-packed-bf16", 512, "fused"), ("t256k-v201k-packed-bf16", 512, "recompute")]
+    assert all(x["status"] == "FAILED" and "needs a GPU" in x["error"] for x in rows)
